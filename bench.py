@@ -1,0 +1,233 @@
+"""Benchmark: one MoE layer, forward + backward, on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: router GEMM
++ softmax + top-K, capacity drop and maps, permute, grouped SwiGLU expert FFN (gate/up
+and down), gate-weighted un-permute, then the backward duals (un-permute backward,
+down dgrad + SwiGLU backward, the two wgrads, gate/up dgrad, router backward, permute
+backward).  The workload is the Mixtral-8x22B-shaped layer: T = 4096 tokens (one
+4096-token sub-sequence), d = 6144, E = 8, top-2, SwiGLU ffn 16384, capacity factor
+1.0, bf16 with fp32 accumulation, seeded synthetic inputs already resident in HBM.
+
+Prints one JSON line.  `roofline` is for the grouped GEMM (the six launches of the
+matrix-core GEMM kernel per step, 18 * n_kept * d * f FLOPs), timed with HIP events
+on the stream the kernels run on; `hbm_kernels` gives the same for the row-movement
+calls; `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec fwd+bwd on 1 MI355X; grouped-GEMM % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events around the ABI calls of one step, on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.acc = {}
+        self.on = False
+
+    def __call__(self, name, fn, *a, **kw):
+        if not self.on:
+            return fn(*a, **kw)
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn(*a, **kw)
+        e.record()
+        self.acc.setdefault(name, []).append((s, e))
+
+    def means_ms(self):
+        self.torch.cuda.synchronize()
+        return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.acc.items()}
+
+
+def run_step(lay, inp, L, tm):
+    """The layer's ABI calls in order, each bracketed by the timer."""
+    b, rt = lay.buf, lay.rt
+    tm("route", L.moe_route, lay.desc, inp["x"], inp["w_router"], inp.get("bias"),
+       inp.get("w_sg"), b["logits"], b["sg_logit"], lay.routing, lay.ws_route)
+    tm("permute", L.moe_permute, lay.desc, inp["x"], lay.routing, b["xp"])
+    tm("ffn_fwd", L.moe_expert_ffn_fwd, lay.desc, b["xp"], inp["w_gate"], inp["w_up"],
+       inp["w_down"], rt["offsets"], b["a"], b["b"], b["h"], b["o"], None)
+    if lay.fs:
+        tm("shared_fwd", L.moe_expert_ffn_fwd, lay.sdesc, inp["x"], inp["ws_gate"], inp["ws_up"],
+           inp["ws_down"], b["shared_offsets"], b["sa"], b["sb"], b["sh"], b["shared"], None)
+    tm("unpermute", L.moe_unpermute, lay.desc, b["o"], lay.routing, b.get("shared"),
+       b["sg_logit"], b["y"])
+    tm("unpermute_bwd", L.moe_unpermute_bwd, lay.desc, inp["dy"], b["o"], lay.routing,
+       b.get("shared"), b["sg_logit"], b["d_o"], b["dgate"], b.get("dshared"), b.get("dz"))
+    tm("ffn_bwd", L.moe_expert_ffn_bwd, lay.desc, b["xp"], b["a"], b["b"], b["h"],
+       inp["w_gate"], inp["w_up"], inp["w_down"], rt["offsets"], b["d_o"], b["dxp"],
+       b["dw_gate"], b["dw_up"], b["dw_down"], lay.ws_ffn)
+    if lay.fs:
+        tm("shared_bwd", L.moe_expert_ffn_bwd, lay.sdesc, inp["x"], b["sa"], b["sb"], b["sh"],
+           inp["ws_gate"], inp["ws_up"], inp["ws_down"], b["shared_offsets"], b["dshared"],
+           b["dx_shared"], b["dws_gate"], b["dws_up"], b["dws_down"], lay.ws_ffn)
+    tm("route_bwd", L.moe_route_bwd, lay.desc, inp["x"], lay.routing, b["dgate"], b.get("dz"),
+       b["dlogits"], b["dw_router"], b.get("dw_sg"), lay.ws_route_bwd)
+    tm("permute_bwd", L.moe_permute_bwd, lay.desc, b["dxp"], lay.routing, b["dlogits"],
+       inp["w_router"], b.get("dz"), inp.get("w_sg"), b.get("dx_shared"), b["dx"],
+       lay.ws_permute_bwd)
+
+
+def cpu_baseline(shape, inp, lay, cap):
+    """Time the CPU oracle on a bounded sample: the routing of all T tokens, the row
+    movement of all T tokens, and the expert FFN forward + backward of expert 0's kept
+    rows; the expert part is scaled by E (experts have near-equal loads here)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    K, E, T = shape.K, shape.E, shape.T
+    logits = lay.buf["logits"].cpu().numpy()
+    t0 = time.perf_counter()
+    r = oracle.route(logits, K, shape.sub_seq, cap)
+    t_route = time.perf_counter() - t0
+
+    x = inp["x"].float().cpu().numpy()
+    dy = inp["dy"].float().cpu().numpy()
+    t0 = time.perf_counter()
+    xp = oracle.permute(x, r["src_of"], K)
+    o_stub = xp  # the row movement costs the same whatever the rows hold
+    y = oracle.unpermute(o_stub, r["row_of"], r["topk_gate"], r["keep"], "bf16")
+    ub = oracle.unpermute_bwd(dy, o_stub, r["row_of"], r["topk_gate"], r["keep"], r["n_kept"],
+                              "bf16")
+    dx = oracle.permute_bwd(ub["d_o"], r["row_of"], r["keep"], T, "bf16")
+    t_rows = time.perf_counter() - t0
+    del y, dx
+
+    lo, hi = int(r["offsets"][0]), int(r["offsets"][1])
+    wg = inp["w_gate"][0:1].float().cpu().numpy()
+    wu = inp["w_up"][0:1].float().cpu().numpy()
+    wd = inp["w_down"][0:1].float().cpu().numpy()
+    off = np.array([0, hi - lo])
+    t0 = time.perf_counter()
+    a, b, h, o = oracle.expert_ffn_fwd(xp[lo:hi], wg, wu, wd, off, "bf16")
+    fb = oracle.expert_ffn_bwd(xp[lo:hi], a, b, h, wg, wu, wd, off, ub["d_o"][lo:hi], "bf16")
+    t_exp = time.perf_counter() - t0
+    del fb
+    total = t_route + t_rows + E * t_exp
+    return {"value": T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"routing + row movement of all {T} tokens ({t_route + t_rows:.2f} s) and "
+                       f"the expert FFN fwd+bwd of expert 0's {hi - lo} kept rows "
+                       f"({t_exp:.2f} s), the expert part scaled x{E}"),
+            "seconds": round(total, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_8x22b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's MoE layer; --gpus {args.gpus} is not supported "
+              "(the cross-GPU exchanges are not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_synth
+    from token_dispatch_expert_router_amd import _lib as L
+    from token_dispatch_expert_router_amd.layer import MoELayer
+
+    L.load()
+    shape = moe_synth.shape_by_name(args.workload)
+    cap = L.moe_capacity(shape.sub_seq, shape.K, shape.E, shape.cf) if shape.cf is not None else -1
+    log(f"bench: workload {shape.name}, drawing inputs on the GPU")
+    inp = moe_synth.make_inputs(shape, device="cuda")
+    lay = MoELayer(shape.T, shape.d, shape.E, shape.K, shape.f, shape.sub_seq, cap,
+                   shape.torch_dtype, fs=shape.fs, device="cuda")
+    tm = Timer(torch)
+    for i in range(args.warmup):
+        run_step(lay, inp, L, tm)
+    torch.cuda.synchronize()
+    log(f"bench: {args.warmup} warmup steps done")
+    n_kept = int(lay.rt["n_kept"].item())
+
+    tm.on = True
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run_step(lay, inp, L, tm)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1000.0 / args.steps
+    calls = tm.means_ms()
+    log(f"bench: {args.steps} timed steps, {ms:.3f} ms/step; per call (ms): "
+        + ", ".join(f"{k} {v:.3f}" for k, v in calls.items()))
+
+    T, d, E, K, f, fs = shape.T, shape.d, shape.E, shape.K, shape.f, shape.fs
+    gemm_flops = 18.0 * n_kept * d * f + (18.0 * T * d * fs if fs else 0.0)
+    router_flops = 6.0 * T * d * E
+    gemm_ms = calls["ffn_fwd"] + calls["ffn_bwd"] + calls.get("shared_fwd", 0) + calls.get(
+        "shared_bwd", 0)
+    achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    s = 2  # bytes per bf16 element
+    hbm_bytes = {
+        "permute": (T + n_kept) * d * s + 4 * n_kept,
+        "unpermute": (n_kept + T) * d * s + 8 * T * K + (T * d * s if fs else 0),
+        "unpermute_bwd": (T + 2 * n_kept) * d * s + 12 * T * K,
+        "permute_bwd": (n_kept + T) * d * s + 4 * T * K,
+    }
+    hbm = {k: {"bytes": v, "ms": round(calls[k], 4),
+               "GBs": round(v / (calls[k] * 1e-3) / 1e9, 1),
+               "frac": round(v / (calls[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+           for k, v in hbm_bytes.items()}
+    hb_tot = sum(hbm_bytes.values())
+    hb_ms = sum(calls[k] for k in hbm_bytes)
+    rec = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": T, "d": d, "E": E, "K": K, "ffn": f,
+                   "shared_ffn": fs, "sub_seq": shape.sub_seq, "capacity_factor": shape.cf,
+                   "capacity": cap, "n_kept": n_kept, "parallelism": "none (1 GPU)"},
+        "tflops": round((gemm_flops + router_flops) / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "gg_mfma_kernel (6 launches per step: fwd gate/up, fwd down, "
+                               "dgrad down, wgrad down, wgrad gate/up, dgrad gate/up)",
+                     "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4)},
+        "hbm_kernels": {"bytes": hb_tot, "ms": round(hb_ms, 4),
+                        "GBs": round(hb_tot / (hb_ms * 1e-3) / 1e9, 1),
+                        "frac": round(hb_tot / (hb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "calls": hbm},
+        "calls_ms": {k: round(v, 4) for k, v in calls.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a bounded sample")
+        rec["cpu_baseline"] = cpu_baseline(shape, inp, lay, cap)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

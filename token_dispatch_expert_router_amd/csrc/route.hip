@@ -1,0 +1,492 @@
+// Router: logits GEMM, softmax, wavefront top-K, capacity drop and permutation maps.
+//
+// "MoE Parallel Folding" (arXiv 2504.14960), knowledge-base notes page, method
+// paragraph: the router assigns each token to its Top-K experts and a permutation
+// makes one expert's tokens contiguous; Section 3.3 Token Dispatcher: assignments
+// over capacity are dropped inside each sub-sequence.  Decisions are integer
+// functions of fp32 values, so every floating-point step of the softmax is written
+// out with its own rounding: no contraction (this file is built with
+// -ffp-contract=off and the pragma below), IEEE division, pairwise sums.
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------------------------
+// exp for r <= 0: Cody & Waite range reduction (Software Manual for the Elementary
+// Functions, 1980) with ln 2 = C1 + C2, C1 = ln 2 truncated to a multiple of 2^-16
+// so n*C1 is exact, then the degree-7 Taylor polynomial in Horner form and an exact
+// scaling by 2^n.  Results below 2^-125 are flushed to +0 (no denormal is made).
+// ---------------------------------------------------------------------------------
+constexpr double kLn2 = 0.69314718055994530942;
+constexpr float kC1 = (float)(45426.0 / 65536.0);
+constexpr float kC2 = (float)(kLn2 - 45426.0 / 65536.0);
+constexpr float kInvLn2 = (float)(1.0 / kLn2);
+
+__device__ __forceinline__ float route_exp(float r) {
+    float t = r * kInvLn2;
+    float n = __builtin_rintf(t);
+    if (n < -125.0f) return 0.0f;
+    float rr = r - n * kC1;
+    rr = rr - n * kC2;
+    float q = (float)(1.0 / 5040.0);
+    q = q * rr + (float)(1.0 / 720.0);
+    q = q * rr + (float)(1.0 / 120.0);
+    q = q * rr + (float)(1.0 / 24.0);
+    q = q * rr + (float)(1.0 / 6.0);
+    q = q * rr + 0.5f;
+    q = q * rr + 1.0f;
+    q = q * rr + 1.0f;
+    return q * __uint_as_float((uint32_t)((int)n + 127) << 23);
+}
+
+__device__ __forceinline__ int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Sum over lanes [0, P) by an xor butterfly (P a power of two): every lane of the
+// group ends with the pairwise-tree sum ((v0+v1)+(v2+v3))+..., the same value on
+// every lane because fp addition is commutative.
+__device__ __forceinline__ float butterfly_sum(float v, int P) {
+    for (int m = 1; m < P; m <<= 1) v = v + __shfl_xor(v, m, MOE_WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, MOE_WAVE));
+    return v;
+}
+
+// Softmax over E logits held one per lane (lane < E), top-K by (p desc, e asc),
+// gates renormalised over the K chosen.  Writes the token's K slots.
+__device__ void softmax_topk_token(float logit, int E, int K, int64_t t,
+                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
+                                   float* __restrict__ topk_gate) {
+    const int lane = threadIdx.x & 63;
+    const bool on = lane < E;
+    float l = on ? logit : -INFINITY;
+    float m = wave_max(l);
+    float u = on ? route_exp(l - m) : 0.0f;
+    float Z = butterfly_sum(u, next_pow2(E));
+    float p = on ? u / Z : 0.0f;
+
+    // K rounds of a wave-wide max over the 64-bit key (p bits, 0xFFFF - e).
+    uint32_t khi = on ? __float_as_uint(p) : 0u;
+    uint32_t klo = on ? (0xFFFFu - (uint32_t)lane) : 0u;
+    int sel_e = 0;
+    float sel_p = 0.0f;
+    for (int k = 0; k < K; ++k) {
+        uint32_t bh = khi, bl = klo;
+#pragma unroll
+        for (int msk = 32; msk >= 1; msk >>= 1) {
+            uint32_t oh = __shfl_xor(bh, msk, MOE_WAVE);
+            uint32_t ol = __shfl_xor(bl, msk, MOE_WAVE);
+            bool take = (oh > bh) || (oh == bh && ol > bl);
+            bh = take ? oh : bh;
+            bl = take ? ol : bl;
+        }
+        int e = (int)(0xFFFFu - bl);
+        if (lane == e) { khi = 0u; klo = 0u; }
+        if (lane == k) { sel_e = e; sel_p = __uint_as_float(bh); }
+    }
+    float P = butterfly_sum(lane < K ? sel_p : 0.0f, next_pow2(K));
+    if (lane < K) {
+        topk_idx[t * K + lane] = sel_e;
+        topk_prob[t * K + lane] = sel_p;
+        topk_gate[t * K + lane] = sel_p / P;
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Router GEMM, bf16 on MFMA: a block of 4 waves takes 16 tokens; the waves split d
+// (split-K) and each computes 16 tokens x 16*NB expert columns with
+// v_mfma_f32_16x16x32_bf16; the four partial sums are added in a fixed order in LDS.
+// Column E (if present) is the shared expert's gate vector w_sg.
+// ---------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int RT_TOK = 16;     // tokens per block
+constexpr int RT_NBMAX = 5;    // up to 80 columns (64 experts + shared gate)
+
+// w_rt: [NB*16][d] bf16, the router weight transposed (row e = column e of w_router,
+// row E = w_sg, zero rows after).
+__global__ void __launch_bounds__(256) transpose_router_w(const bf16_t* __restrict__ w,
+                                                          const bf16_t* __restrict__ w_sg,
+                                                          bf16_t* __restrict__ w_rt, int d,
+                                                          int E, int ncol) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)ncol * d) return;
+    int e = (int)(i / d);
+    int k = (int)(i % d);
+    bf16_t v = 0;
+    if (e < E) v = w[(int64_t)k * E + e];
+    else if (e == E && w_sg) v = w_sg[k];
+    w_rt[i] = v;
+}
+
+__global__ void __launch_bounds__(256) router_fwd_mfma(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_rt, const float* __restrict__ bias,
+    float* __restrict__ logits, float* __restrict__ sg_logit, int T, int d, int E, int K,
+    int NB, int has_sg, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
+    float* __restrict__ topk_gate) {
+    __shared__ float part[4][RT_TOK][RT_NBMAX * 16 + 1];
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int t0 = blockIdx.x * RT_TOK;
+    const int row = lane & 15;      // token within the block (A) / column (B)
+    const int kq = lane >> 4;       // which 8-wide k group of the 32
+    const int dslice = d / 4;
+    const int kbeg = wave * dslice;
+
+    f32x4_t acc[RT_NBMAX];
+#pragma unroll
+    for (int j = 0; j < RT_NBMAX; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int tok = t0 + row;
+    const bool tok_ok = tok < T;
+    const bf16_t* xa = x + (int64_t)(tok_ok ? tok : 0) * d + kbeg + kq * 8;
+    for (int k = 0; k < dslice; k += 32) {
+        u32x4 av = tok_ok ? *(const u32x4*)(xa + k) : u32x4{0, 0, 0, 0};
+        bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int j = 0; j < RT_NBMAX; ++j) {
+            if (j < NB) {
+                const bf16_t* wb = w_rt + (int64_t)(j * 16 + row) * d + kbeg + kq * 8 + k;
+                bf16x8_t b = __builtin_bit_cast(bf16x8_t, *(const u32x4*)wb);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+            }
+        }
+    }
+    // D layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4)+i.
+#pragma unroll
+    for (int j = 0; j < RT_NBMAX; ++j) {
+        if (j < NB) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[wave][4 * kq + i][j * 16 + row] = acc[j][i];
+        }
+    }
+    __syncthreads();
+    // Each wave finishes 4 tokens: fixed-order sum of the 4 split-K partials, bias,
+    // then softmax and top-K with one lane per expert.
+    for (int q = 0; q < RT_TOK / 4; ++q) {
+        int tl = wave * (RT_TOK / 4) + q;
+        int t = t0 + tl;
+        if (t >= T) break;
+        float l = 0.f;
+        if (lane < E + has_sg) {
+            l = ((part[0][tl][lane] + part[1][tl][lane]) + part[2][tl][lane]) + part[3][tl][lane];
+            if (lane < E && bias) l = l + bias[lane];
+            if (lane < E) logits[(int64_t)t * E + lane] = l;
+            else sg_logit[t] = l;
+        }
+        softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
+    }
+}
+
+// Generic router (fp32, or bf16 with d % 128 != 0): one wave per token.
+template <typename T>
+__global__ void __launch_bounds__(64) router_fwd_valu(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ bias,
+    const T* __restrict__ w_sg, float* __restrict__ logits, float* __restrict__ sg_logit,
+    int d, int E, int K, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
+    float* __restrict__ topk_gate) {
+    __shared__ float lg[65];
+    const int lane = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    const int ncol = E + (w_sg ? 1 : 0);
+    for (int e = 0; e < ncol; ++e) {
+        float s = 0.f;
+        for (int k = lane; k < d; k += 64) {
+            float wv = (e < E) ? Elem<T>::load(w, (int64_t)k * E + e) : Elem<T>::load(w_sg, k);
+            s += Elem<T>::load(x, t * d + k) * wv;
+        }
+        s = wave_sum(s);
+        if (lane == 0) lg[e] = s;
+    }
+    __syncthreads();
+    float l = 0.f;
+    if (lane < ncol) {
+        l = lg[lane];
+        if (lane < E && bias) l = l + bias[lane];
+        if (lane < E) logits[t * E + lane] = l;
+        else sg_logit[t] = l;
+    }
+    softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
+}
+
+__global__ void __launch_bounds__(256) topk_from_logits(const float* __restrict__ logits, int T,
+                                                        int E, int K,
+                                                        int32_t* __restrict__ topk_idx,
+                                                        float* __restrict__ topk_prob,
+                                                        float* __restrict__ topk_gate) {
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    float l = lane < E ? logits[t * E + lane] : 0.f;
+    softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
+}
+
+// ---------------------------------------------------------------------------------
+// Capacity drop, one block per (sub-sequence s, expert e).  The candidates are the
+// tokens of the sub-sequence that chose e (at most one slot each), collected in
+// token order.  If there are more than `capacity`, the kept ones are the capacity
+// largest under (p desc, t asc): a 4-pass radix select on the fp32 bit pattern of
+// p (order-preserving for p >= 0) finds the threshold value and how many of the
+// candidates equal to it are kept; those are the first ones in token order.
+// ---------------------------------------------------------------------------------
+constexpr int SEL_THREADS = 256;
+
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
+    // sh: >= 8 ints of shared memory
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int n = __shfl_up(incl, o, MOE_WAVE);
+        if (lane >= o) incl += n;
+    }
+    __syncthreads();
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < SEL_THREADS / 64; ++w) {
+        if (w < wave) base += sh[w];
+        tot += sh[w];
+    }
+    *total = tot;
+    return base + incl - v;
+}
+
+__global__ void __launch_bounds__(SEL_THREADS) select_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_prob, int S, int E,
+    int K, int capacity, uint8_t* __restrict__ keep, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ routed_counts, int32_t* __restrict__ kcnt, int32_t* __restrict__ cand,
+    int32_t* __restrict__ kept_list) {
+    __shared__ int sh_scan[8];
+    __shared__ int hist[256];
+    __shared__ int sh_digit, sh_above;
+    const int s = blockIdx.y;
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int per = (S + SEL_THREADS - 1) / SEL_THREADS;
+    const int64_t tbeg = (int64_t)s * S + (int64_t)tid * per;
+    const int64_t tend = min(tbeg + per, (int64_t)(s + 1) * S);
+    const int64_t g = (int64_t)s * E + e;
+    int32_t* my_cand = cand + g * S;
+    int32_t* my_kept = kept_list + g * S;
+
+    int c = 0;
+    for (int64_t t = tbeg; t < tend; ++t)
+        for (int k = 0; k < K; ++k)
+            if (topk_idx[t * K + k] == e) ++c;
+    int n;
+    int base = block_exclusive_scan(c, sh_scan, &n);
+    {
+        int w = base;
+        for (int64_t t = tbeg; t < tend; ++t)
+            for (int k = 0; k < K; ++k)
+                if (topk_idx[t * K + k] == e) my_cand[w++] = (int32_t)(t * K + k);
+    }
+    if (tid == 0) routed_counts[g] = n;
+
+    // Threshold (bits of the capacity-th largest p) and how many equal to it to keep.
+    uint32_t thr = 0u;
+    int want_eq = 0;
+    const bool all_kept = capacity < 0 || n <= capacity;
+    const bool none_kept = !all_kept && capacity == 0;
+    if (!all_kept && !none_kept) {
+        uint32_t prefix = 0u, pmask = 0u;
+        int want = capacity;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+            __syncthreads();
+            for (int i = base; i < base + c; ++i) {
+                uint32_t key = __float_as_uint(topk_prob[my_cand[i]]);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // lane l owns digits 255-4l .. 252-4l (descending)
+                int hv[4];
+                int loc = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { hv[j] = hist[255 - 4 * tid - j]; loc += hv[j]; }
+                int incl = loc;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    int nb = __shfl_up(incl, o, MOE_WAVE);
+                    if (tid >= o) incl += nb;
+                }
+                int excl = incl - loc;  // count of digits above this lane's four
+                bool hit = excl < want && incl >= want;
+                if (hit) {
+                    int run = excl;
+                    for (int j = 0; j < 4; ++j) {
+                        if (run + hv[j] >= want) {
+                            sh_digit = 255 - 4 * tid - j;
+                            sh_above = run;
+                            break;
+                        }
+                        run += hv[j];
+                    }
+                }
+            }
+            __syncthreads();
+            want -= sh_above;
+            prefix |= ((uint32_t)sh_digit) << shift;
+            pmask |= 255u << shift;
+            __syncthreads();
+        }
+        thr = prefix;
+        want_eq = want;
+    }
+
+    // Keep flags, in token order; equal-to-threshold candidates ranked by token.
+    int eq_local = 0;
+    if (!all_kept && !none_kept)
+        for (int i = base; i < base + c; ++i)
+            if (__float_as_uint(topk_prob[my_cand[i]]) == thr) ++eq_local;
+    int eq_tot;
+    int eq_base = block_exclusive_scan(eq_local, sh_scan, &eq_tot);
+    int kc = 0;
+    {
+        int eq_seen = eq_base;
+        for (int i = base; i < base + c; ++i) {
+            int slot = my_cand[i];
+            bool kp;
+            if (all_kept) kp = true;
+            else if (none_kept) kp = false;
+            else {
+                uint32_t key = __float_as_uint(topk_prob[slot]);
+                if (key > thr) kp = true;
+                else if (key == thr) kp = (eq_seen++ < want_eq);
+                else kp = false;
+            }
+            keep[slot] = kp ? 1 : 0;
+            if (!kp) row_of[slot] = -1;
+            kc += kp ? 1 : 0;
+        }
+    }
+    int ktot;
+    int kbase = block_exclusive_scan(kc, sh_scan, &ktot);
+    {
+        int w = kbase;
+        for (int i = base; i < base + c; ++i) {
+            int slot = my_cand[i];
+            if (keep[slot]) my_kept[w++] = slot;
+        }
+    }
+    if (tid == 0) kcnt[g] = ktot;
+}
+
+// Rows of every kept assignment: experts in ascending order, then tokens ascending
+// (sub-sequences in order, token order inside each).  One block per (s, e).
+__global__ void __launch_bounds__(256) maps_kernel(const int32_t* __restrict__ kcnt,
+                                                   const int32_t* __restrict__ kept_list,
+                                                   int n_sub, int S, int E,
+                                                   int32_t* __restrict__ row_of,
+                                                   int32_t* __restrict__ src_of,
+                                                   int32_t* __restrict__ kept_counts,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ n_kept) {
+    __shared__ int red[4];
+    const int s = blockIdx.y;
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    // base = kept rows of experts < e (all sub-sequences) + of expert e in sub-seqs < s
+    int part = 0;
+    for (int i = tid; i < n_sub * E; i += 256) {
+        int ss = i / E, ee = i % E;
+        if (ee < e || (ee == e && ss < s)) part += kcnt[i];
+    }
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o, MOE_WAVE);
+    if ((tid & 63) == 0) red[tid >> 6] = part;
+    __syncthreads();
+    const int base = red[0] + red[1] + red[2] + red[3];
+    const int64_t g = (int64_t)s * E + e;
+    const int cnt = kcnt[g];
+    const int32_t* lst = kept_list + g * S;
+    for (int j = tid; j < cnt; j += 256) {
+        int slot = lst[j];
+        src_of[base + j] = slot;
+        row_of[slot] = base + j;
+    }
+    if (s == 0 && e == 0 && tid < 64) {
+        // kept counts per expert and their exclusive scan (E <= 64: one lane each)
+        int kc = 0;
+        if (tid < E)
+            for (int ss = 0; ss < n_sub; ++ss) kc += kcnt[(int64_t)ss * E + tid];
+        int incl = kc;
+        for (int o = 1; o < 64; o <<= 1) {
+            int nb = __shfl_up(incl, o, MOE_WAVE);
+            if (tid >= o) incl += nb;
+        }
+        if (tid < E) {
+            kept_counts[tid] = kc;
+            offsets[tid] = incl - kc;
+        }
+        if (tid == E - 1) {
+            offsets[E] = incl;
+            n_kept[0] = incl;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_router_fwd(const moe_desc& d, const void* x, const void* w_router,
+                             const float* bias, const void* w_sg, float* logits,
+                             float* sg_logit, const moe_routing& r, hipStream_t s,
+                             void* w_rt_ws) {
+    const int ncol = d.E + (w_sg ? 1 : 0);
+    if (d.dtype == MOE_BF16 && d.d % 128 == 0 && w_rt_ws) {
+        const int NB = (ncol + 15) / 16;
+        bf16_t* wrt = (bf16_t*)w_rt_ws;
+        int64_t n = (int64_t)NB * 16 * d.d;
+        transpose_router_w<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            (const bf16_t*)w_router, (const bf16_t*)w_sg, wrt, d.d, d.E, NB * 16);
+        router_fwd_mfma<<<(d.T + RT_TOK - 1) / RT_TOK, 256, 0, s>>>(
+            (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB, w_sg ? 1 : 0,
+            r.topk_idx, r.topk_prob, r.topk_gate);
+    } else if (d.dtype == MOE_BF16) {
+        router_fwd_valu<bf16_t><<<d.T, 64, 0, s>>>(
+            (const bf16_t*)x, (const bf16_t*)w_router, bias, (const bf16_t*)w_sg, logits, sg_logit,
+            d.d, d.E, d.K, r.topk_idx, r.topk_prob, r.topk_gate);
+    } else {
+        router_fwd_valu<float><<<d.T, 64, 0, s>>>(
+            (const float*)x, (const float*)w_router, bias, (const float*)w_sg, logits, sg_logit,
+            d.d, d.E, d.K, r.topk_idx, r.topk_prob, r.topk_gate);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_from_logits(const moe_desc& d, const float* logits, const moe_routing& r,
+                                   hipStream_t s) {
+    topk_from_logits<<<(d.T + 3) / 4, 256, 0, s>>>(logits, d.T, d.E, d.K, r.topk_idx,
+                                                   r.topk_prob, r.topk_gate);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_and_maps(const moe_desc& d, const moe_routing& r, RouteWs ws,
+                                  hipStream_t s) {
+    const int n_sub = d.T / d.sub_seq;
+    dim3 grid(d.E, n_sub);
+    int32_t* cand = ws.list;
+    int32_t* kept = ws.list + (int64_t)n_sub * d.E * d.sub_seq;
+    select_kernel<<<grid, SEL_THREADS, 0, s>>>(r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K,
+                                               d.capacity, r.keep, r.row_of, r.routed_counts,
+                                               ws.kcnt, cand, kept);
+    maps_kernel<<<grid, 256, 0, s>>>(ws.kcnt, kept, n_sub, d.sub_seq, d.E, r.row_of, r.src_of,
+                                     r.kept_counts, r.offsets, r.n_kept);
+    return hipGetLastError();
+}
+
+}  // namespace moe

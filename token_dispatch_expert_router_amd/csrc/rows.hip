@@ -1,0 +1,401 @@
+// Row movement of the dispatcher and its backward duals, plus the router backward.
+//
+// "MoE Parallel Folding" (arXiv 2504.14960), knowledge-base notes page, method
+// paragraph: permutation gathers each expert's tokens into a contiguous block, the
+// un-permutation restores token order, and the backward pass runs the duals.  These
+// kernels are pure HBM streams: every row is moved with 16-byte vector accesses,
+// one wavefront per row, with several loads in flight per lane.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 4 waves per block
+constexpr int UNROLL = 4;
+
+// xp[r] = x[src_of[r] / K] for r < n_kept.
+__global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ x,
+                                                      const int32_t* __restrict__ src_of,
+                                                      const int32_t* __restrict__ n_kept, int K,
+                                                      int vpr, u32x4* __restrict__ xp) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (r >= n_kept[0]) return;
+    const int64_t t = src_of[r] / K;
+    const u32x4* src = x + t * vpr;
+    u32x4* dst = xp + r * vpr;
+    int c = lane;
+    for (; c + 64 * (UNROLL - 1) < vpr; c += 64 * UNROLL) {
+        u32x4 v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = src[c + 64 * u];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) dst[c + 64 * u] = v[u];
+    }
+    for (; c < vpr; c += 64) dst[c] = src[c];
+}
+
+// y_t = sum_{kept k, ascending} g_tk o[row_of[t,k]]  (+ sigmoid(z_t) shared_t)
+template <typename T>
+__global__ void __launch_bounds__(256) unpermute_kernel(
+    const u32x4* __restrict__ o, const int32_t* __restrict__ row_of,
+    const float* __restrict__ gate, const uint8_t* __restrict__ keep,
+    const u32x4* __restrict__ shared, const float* __restrict__ z, int ntok, int K, int vpr,
+    u32x4* __restrict__ y) {
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    int64_t rows[8];
+    float g[8];
+    int nk = 0;
+    for (int k = 0; k < K; ++k) {
+        if (keep[t * K + k]) {
+            rows[nk] = row_of[t * K + k];
+            g[nk] = gate[t * K + k];
+            ++nk;
+        }
+    }
+    const float s = shared ? sigmoid_f(z[t]) : 0.f;
+    for (int c = lane; c < vpr; c += 64) {
+        float acc[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = 0.f;
+        for (int j = 0; j < nk; ++j) {
+            float v[N];
+            Vec16<T>::unpack(o[rows[j] * vpr + c], v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] += g[j] * v[i];
+        }
+        if (shared) {
+            float v[N];
+            Vec16<T>::unpack(shared[t * vpr + c], v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] += s * v[i];
+        }
+        y[t * vpr + c] = Vec16<T>::pack(acc);
+    }
+}
+
+// d_o[row_of[t,k]] = g_tk dy_t ; dgate_tk = <dy_t, o[row_of[t,k]]> ;
+// shared: dshared_t = s_t dy_t, dz_t = <dy_t, shared_t> s_t (1 - s_t).
+template <typename T>
+__global__ void __launch_bounds__(256) unpermute_bwd_kernel(
+    const u32x4* __restrict__ dy, const u32x4* __restrict__ o, const int32_t* __restrict__ row_of,
+    const float* __restrict__ gate, const uint8_t* __restrict__ keep,
+    const u32x4* __restrict__ shared, const float* __restrict__ z, int ntok, int K, int vpr,
+    u32x4* __restrict__ d_o, float* __restrict__ dgate, u32x4* __restrict__ dshared,
+    float* __restrict__ dz) {
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    int64_t rows[8];
+    float g[8];
+    float dot[8];
+    int kk[8];
+    int nk = 0;
+    for (int k = 0; k < K; ++k) {
+        if (keep[t * K + k]) {
+            rows[nk] = row_of[t * K + k];
+            g[nk] = gate[t * K + k];
+            kk[nk] = k;
+            dot[nk] = 0.f;
+            ++nk;
+        } else if (lane == 0) {
+            dgate[t * K + k] = 0.f;
+        }
+    }
+    const float s = shared ? sigmoid_f(z[t]) : 0.f;
+    float sdot = 0.f;
+    for (int c = lane; c < vpr; c += 64) {
+        float dv[N];
+        Vec16<T>::unpack(dy[t * vpr + c], dv);
+        for (int j = 0; j < nk; ++j) {
+            float ov[N], w[N];
+            Vec16<T>::unpack(o[rows[j] * vpr + c], ov);
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                acc += dv[i] * ov[i];
+                w[i] = g[j] * dv[i];
+            }
+            dot[j] += acc;
+            d_o[rows[j] * vpr + c] = Vec16<T>::pack(w);
+        }
+        if (shared) {
+            float sv[N], w[N];
+            Vec16<T>::unpack(shared[t * vpr + c], sv);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                sdot += dv[i] * sv[i];
+                w[i] = s * dv[i];
+            }
+            dshared[t * vpr + c] = Vec16<T>::pack(w);
+        }
+    }
+    for (int j = 0; j < nk; ++j) {
+        float v = wave_sum(dot[j]);
+        if (lane == 0) dgate[t * K + kk[j]] = v;
+    }
+    if (shared) {
+        float v = wave_sum(sdot);
+        if (lane == 0) dz[t] = v * s * (1.f - s);
+    }
+}
+
+// w_rt[e][i] = w_router[i][e] (e < E), w_rt[E][i] = w_sg[i]: row access for the
+// router term of dx.
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_rw_kernel(const T* __restrict__ w,
+                                                           const T* __restrict__ w_sg,
+                                                           T* __restrict__ w_rt, int d, int E,
+                                                           int ncol) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)ncol * d) return;
+    int e = (int)(i / d), k = (int)(i % d);
+    T v = 0;
+    if (e < E) {
+        if (w) v = w[(int64_t)k * E + e];
+    } else if (w_sg) {
+        v = w_sg[k];
+    }
+    w_rt[i] = v;
+}
+
+// dx_t = sum_{kept k} dxp[row_of[t,k]] + sum_k dl[t,e_k] w_rt[e_k] + dz_t w_sg + dx_add_t
+template <typename T>
+__global__ void __launch_bounds__(256) permute_bwd_kernel(
+    const u32x4* __restrict__ dxp, const int32_t* __restrict__ row_of,
+    const uint8_t* __restrict__ keep, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dlogits, const u32x4* __restrict__ w_rt,
+    const float* __restrict__ dz, const u32x4* __restrict__ dx_add, int ntok, int E, int K,
+    int vpr, u32x4* __restrict__ dx) {
+    constexpr int N = Vec16<T>::N;
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    if (t >= ntok) return;
+    int64_t rows[8];
+    int nk = 0;
+    for (int k = 0; k < K; ++k)
+        if (keep[t * K + k]) rows[nk++] = row_of[t * K + k];
+    int rexp[9];
+    float rw[9];
+    int nr = 0;
+    if (dlogits) {
+        for (int k = 0; k < K; ++k) {
+            int e = topk_idx[t * K + k];
+            rexp[nr] = e;
+            rw[nr] = dlogits[t * E + e];
+            ++nr;
+        }
+    }
+    if (dz) {
+        rexp[nr] = E;
+        rw[nr] = dz[t];
+        ++nr;
+    }
+    for (int c = lane; c < vpr; c += 64) {
+        float acc[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = 0.f;
+        for (int j = 0; j < nk; ++j) {
+            float v[N];
+            Vec16<T>::unpack(dxp[rows[j] * vpr + c], v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] += v[i];
+        }
+        for (int j = 0; j < nr; ++j) {
+            float v[N];
+            Vec16<T>::unpack(w_rt[(int64_t)rexp[j] * vpr + c], v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] += rw[j] * v[i];
+        }
+        if (dx_add) {
+            float v[N];
+            Vec16<T>::unpack(dx_add[t * vpr + c], v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] += v[i];
+        }
+        dx[t * vpr + c] = Vec16<T>::pack(acc);
+    }
+}
+
+// dl for the K chosen experts: g_j (dgate_j - sum_k g_k dgate_k); 0 elsewhere.
+__global__ void __launch_bounds__(256) dlogits_kernel(const int32_t* __restrict__ topk_idx,
+                                                      const float* __restrict__ gate,
+                                                      const float* __restrict__ dgate, int T,
+                                                      int E, int K, float* __restrict__ dl) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float inner = 0.f;
+    for (int k = 0; k < K; ++k) inner += gate[t * K + k] * dgate[t * K + k];
+    float v = 0.f;
+    for (int k = 0; k < K; ++k)
+        if (topk_idx[t * K + k] == lane) v = gate[t * K + k] * (dgate[t * K + k] - inner);
+    if (lane < E) dl[t * E + lane] = v;
+}
+
+// partial[c][i][e] = sum over tokens t of chunk c of x[t][i] * dcol[t][e], where the
+// columns are dl (e < E) and dz (e == E).  A wave owns 8 consecutive i (one 16-byte
+// x vector per lane... one per token) and 8 columns; chunks are summed in order later.
+template <typename T>
+__global__ void __launch_bounds__(64) router_wgrad_partial(
+    const T* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ dz, int T_,
+    int d, int E, int ncol, int chunk, float* __restrict__ partial) {
+    constexpr int N = Vec16<T>::N;       // i per lane
+    const int lane = threadIdx.x;
+    const int i0 = (blockIdx.x * 64 + lane) * N;
+    const int c = blockIdx.y;
+    const int e0 = blockIdx.z * 8;
+    float acc[N][8];
+#pragma unroll
+    for (int a = 0; a < N; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
+    const bool ok = i0 < d;
+    const int64_t tb = (int64_t)c * chunk;
+    const int64_t te = min(tb + chunk, (int64_t)T_);
+    for (int64_t t = tb; t < te; ++t) {
+        float w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            int e = e0 + b;
+            w[b] = (e < E) ? dl[t * E + e] : ((e == E && dz) ? dz[t] : 0.f);
+        }
+        if (ok) {
+            float xv[N];
+            Vec16<T>::unpack(*(const u32x4*)(x + t * d + i0), xv);
+#pragma unroll
+            for (int a = 0; a < N; ++a)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) acc[a][b] += xv[a] * w[b];
+        }
+    }
+    if (ok) {
+        const int ncol8 = (ncol + 7) / 8 * 8;
+#pragma unroll
+        for (int a = 0; a < N; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                partial[((int64_t)c * d + i0 + a) * ncol8 + e0 + b] = acc[a][b];
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) router_wgrad_final(const float* __restrict__ partial,
+                                                          int n_chunks, int d, int E, int ncol,
+                                                          T* __restrict__ dw, T* __restrict__ dw_sg) {
+    int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int ncol8 = (ncol + 7) / 8 * 8;
+    if (idx >= (int64_t)d * ncol) return;
+    int i = (int)(idx / ncol), e = (int)(idx % ncol);
+    float s = 0.f;
+    for (int c = 0; c < n_chunks; ++c) s += partial[((int64_t)c * d + i) * ncol8 + e];
+    if (e < E) Elem<T>::store(dw, (int64_t)i * E + e, s);
+    else Elem<T>::store(dw_sg, i, s);
+}
+
+inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_permute(const moe_desc& d, int64_t R, const void* x, const moe_routing& r,
+                          void* xp, hipStream_t s) {
+    const int esz = d.dtype == MOE_BF16 ? 2 : 4;
+    const int vpr = d.d * esz / 16;
+    if (R > 0)
+        permute_kernel<<<blocks_for(R, ROWS_PER_BLOCK), 256, 0, s>>>(
+            (const u32x4*)x, r.src_of, r.n_kept, d.K, vpr, (u32x4*)xp);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const moe_desc& d, const void* o, const moe_routing& r,
+                            const void* shared, const float* z, void* y, hipStream_t s) {
+    const int esz = d.dtype == MOE_BF16 ? 2 : 4;
+    const int vpr = d.d * esz / 16;
+    const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
+    if (d.dtype == MOE_BF16)
+        unpermute_kernel<bf16_t><<<nb, 256, 0, s>>>((const u32x4*)o, r.row_of, r.topk_gate, r.keep,
+                                                    (const u32x4*)shared, z, d.T, d.K, vpr,
+                                                    (u32x4*)y);
+    else
+        unpermute_kernel<float><<<nb, 256, 0, s>>>((const u32x4*)o, r.row_of, r.topk_gate, r.keep,
+                                                   (const u32x4*)shared, z, d.T, d.K, vpr,
+                                                   (u32x4*)y);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_bwd(const moe_desc& d, const void* dy, const void* o,
+                                const moe_routing& r, const void* shared, const float* z,
+                                void* d_o, float* dgate, void* dshared, float* dz, hipStream_t s) {
+    const int esz = d.dtype == MOE_BF16 ? 2 : 4;
+    const int vpr = d.d * esz / 16;
+    const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
+    if (d.dtype == MOE_BF16)
+        unpermute_bwd_kernel<bf16_t><<<nb, 256, 0, s>>>(
+            (const u32x4*)dy, (const u32x4*)o, r.row_of, r.topk_gate, r.keep, (const u32x4*)shared,
+            z, d.T, d.K, vpr, (u32x4*)d_o, dgate, (u32x4*)dshared, dz);
+    else
+        unpermute_bwd_kernel<float><<<nb, 256, 0, s>>>(
+            (const u32x4*)dy, (const u32x4*)o, r.row_of, r.topk_gate, r.keep, (const u32x4*)shared,
+            z, d.T, d.K, vpr, (u32x4*)d_o, dgate, (u32x4*)dshared, dz);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_bwd(const moe_desc& d, const void* dxp, const moe_routing& r,
+                              const float* dlogits, const void* w_router, const float* dz,
+                              const void* w_sg, const void* dx_add, void* dx, void* w_rt,
+                              hipStream_t s) {
+    const int esz = d.dtype == MOE_BF16 ? 2 : 4;
+    const int vpr = d.d * esz / 16;
+    const int ncol = d.E + 1;
+    const bool need_rt = dlogits || dz;
+    const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
+    const unsigned tb = blocks_for((int64_t)ncol * d.d, 256);
+    if (d.dtype == MOE_BF16) {
+        if (need_rt)
+            transpose_rw_kernel<bf16_t><<<tb, 256, 0, s>>>(
+                (const bf16_t*)w_router, (const bf16_t*)w_sg, (bf16_t*)w_rt, d.d, d.E, ncol);
+        permute_bwd_kernel<bf16_t><<<nb, 256, 0, s>>>(
+            (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
+            (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
+    } else {
+        if (need_rt)
+            transpose_rw_kernel<float><<<tb, 256, 0, s>>>(
+                (const float*)w_router, (const float*)w_sg, (float*)w_rt, d.d, d.E, ncol);
+        permute_bwd_kernel<float><<<nb, 256, 0, s>>>(
+            (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
+            (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing& r,
+                             const float* dgate, const float* dz, float* dlogits, void* dw_router,
+                             void* dw_sg, float* partial, int n_chunks, int chunk, hipStream_t s) {
+    const int ncol = d.E + (dz ? 1 : 0);
+    const int per = d.dtype == MOE_BF16 ? 8 : 4;
+    dim3 g1(blocks_for(d.d / per, 64), n_chunks, (ncol + 7) / 8);
+    const unsigned g2 = blocks_for((int64_t)d.d * ncol, 256);
+    if (d.T > 0)  // with no token the final pass alone writes zero gradients
+        dlogits_kernel<<<blocks_for(d.T, 4), 256, 0, s>>>(r.topk_idx, r.topk_gate, dgate, d.T,
+                                                           d.E, d.K, dlogits);
+    if (d.dtype == MOE_BF16) {
+        if (n_chunks > 0)
+            router_wgrad_partial<bf16_t><<<g1, 64, 0, s>>>((const bf16_t*)x, dlogits, dz, d.T, d.d,
+                                                            d.E, ncol, chunk, partial);
+        router_wgrad_final<bf16_t><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
+                                                       (bf16_t*)dw_router, (bf16_t*)dw_sg);
+    } else {
+        if (n_chunks > 0)
+            router_wgrad_partial<float><<<g1, 64, 0, s>>>((const float*)x, dlogits, dz, d.T, d.d,
+                                                           d.E, ncol, chunk, partial);
+        router_wgrad_final<float><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
+                                                      (float*)dw_router, (float*)dw_sg);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe
