@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_8x22b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's MoE layer; --gpus {args.gpus} is not supported "
@@ -223,6 +226,15 @@ def main():
                         "calls": hbm},
         "calls_ms": {k: round(v, 4) for k, v in calls.items()},
     }
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["calib_copy_bytes"] = n * 4
+        del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a bounded sample")
         rec["cpu_baseline"] = cpu_baseline(shape, inp, lay, cap)
