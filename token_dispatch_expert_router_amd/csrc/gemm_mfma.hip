@@ -395,68 +395,99 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     }
 
     // Epilogue.  32x32 MFMA result: lane holds column (lane & 31) and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r.
+    // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r.  Each wave stages one
+    // 32-row band of its fp32 results at a time in a private 32 KB of LDS, then every
+    // lane handles 8-column chunks: 16-byte coalesced loads of epilogue inputs and
+    // 16-byte stores (16 lanes cover 256 contiguous bytes of a row).
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the operand stages
+    typedef __attribute__((address_space(3))) float lds_f32;
+    const uint32_t wbase = smem_base + wv * 32768;
     const int cl = lane & 31;
     const int rq = 4 * (lane >> 5);
+    constexpr int P = MODE == GG_FWD_GATEUP ? 68 : 132;  // band row pitch in floats
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int rl = wm * 128 + i * 32 + 8 * (r >> 2) + rq + (r & 3);
-            if (MODE == GG_FWD_GATEUP) {
-                const int row = m0 + rl;
+        for (int j = 0; j < 4; ++j) {
+            // gate/up: columns j = 0, 1 are a (first buffer), j = 2, 3 are b (second)
+            const uint32_t buf = (MODE == GG_FWD_GATEUP && j >= 2) ? wbase + 32 * P * 4 : wbase;
+            const int col = (MODE == GG_FWD_GATEUP ? (j & 1) : j) * 32 + cl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rl = 8 * (r >> 2) + rq + (r & 3);
+                *(lds_f32*)(uintptr_t)(buf + (rl * P + col) * 4) = acc[i][j][r];
+            }
+        }
+        const int row_base = wm * 128 + i * 32;  // within the block tile
+        if (MODE == GG_FWD_GATEUP) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int q = lane + 64 * t;
+                const int rl = q >> 3, cc = q & 7;
+                const int row = m0 + row_base + rl;
+                const uint32_t la = wbase + (rl * P + cc * 8) * 4;
+                const uint32_t lb = la + 32 * P * 4;
+                u32x4_t a0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)la;
+                u32x4_t a1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(la + 16);
+                u32x4_t b0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)lb;
+                u32x4_t b1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(lb + 16);
                 if (row < m_lim) {
+                    float av[8], bv[8], hv[8];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int col = n0 + wn * 64 + j * 32 + cl;
-                        const float a = acc[i][j][r], b = acc[i][j + 2][r];
-                        const float h = a * fast_sigmoid(a) * b;
-                        const int64_t o = (int64_t)row * f + col;
-                        ((bf16_t*)g.C0)[o] = f32_to_bf16(a);
-                        ((bf16_t*)g.C1)[o] = f32_to_bf16(b);
-                        ((bf16_t*)g.C2)[o] = f32_to_bf16(h);
+                    for (int u = 0; u < 4; ++u) {
+                        av[u] = __uint_as_float(a0[u]); av[u + 4] = __uint_as_float(a1[u]);
+                        bv[u] = __uint_as_float(b0[u]); bv[u + 4] = __uint_as_float(b1[u]);
                     }
-                }
-            } else if (MODE == GG_FWD_DOWN || MODE == GG_DGRAD_GATEUP) {
-                const int row = m0 + rl;
-                if (row < m_lim) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int col = n0 + wn * 128 + j * 32 + cl;
-                        ((bf16_t*)g.C0)[(int64_t)row * d + col] = f32_to_bf16(acc[i][j][r]);
+                    for (int u = 0; u < 8; ++u) hv[u] = av[u] * fast_sigmoid(av[u]) * bv[u];
+                    const int64_t o = (int64_t)row * f + n0 + wn * 64 + cc * 8;
+                    *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(av);
+                    *(u32x4*)((bf16_t*)g.C1 + o) = Vec16<bf16_t>::pack(bv);
+                    *(u32x4*)((bf16_t*)g.C2 + o) = Vec16<bf16_t>::pack(hv);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int q = lane + 64 * t;
+                const int rl = q >> 4, cc = q & 15;
+                const uint32_t la = wbase + (rl * P + cc * 8) * 4;
+                u32x4_t v0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)la;
+                u32x4_t v1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(la + 16);
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) { v[u] = __uint_as_float(v0[u]); v[u + 4] = __uint_as_float(v1[u]); }
+                const int rt = row_base + rl;              // row within the block tile
+                const int ct = wn * 128 + cc * 8;          // column within the block tile
+                if (MODE == GG_FWD_DOWN || MODE == GG_DGRAD_GATEUP) {
+                    const int row = m0 + rt;
+                    if (row < m_lim)
+                        *(u32x4*)((bf16_t*)g.C0 + (int64_t)row * d + n0 + ct) = Vec16<bf16_t>::pack(v);
+                } else if (MODE == GG_DGRAD_DOWN) {
+                    const int row = m0 + rt;
+                    if (row < m_lim) {
+                        const int64_t o = (int64_t)row * f + n0 + ct;
+                        float av[8], bv[8], dav[8], dbv[8];
+                        Vec16<bf16_t>::unpack(*(const u32x4*)((const bf16_t*)g.X0 + o), av);
+                        Vec16<bf16_t>::unpack(*(const u32x4*)((const bf16_t*)g.X1 + o), bv);
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) {
+                            const float sg = fast_sigmoid(av[u]);
+                            dav[u] = v[u] * bv[u] * sg * (1.0f + av[u] * (1.0f - sg));
+                            dbv[u] = v[u] * av[u] * sg;
+                        }
+                        *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(dav);
+                        *(u32x4*)((bf16_t*)g.C1 + o) = Vec16<bf16_t>::pack(dbv);
                     }
-                }
-            } else if (MODE == GG_DGRAD_DOWN) {
-                const int row = m0 + rl;
-                if (row < m_lim) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int col = n0 + wn * 128 + j * 32 + cl;
-                        const int64_t o = (int64_t)row * f + col;
-                        const float dh = acc[i][j][r];
-                        const float a = bf16_to_f32(((const bf16_t*)g.X0)[o]);
-                        const float b = bf16_to_f32(((const bf16_t*)g.X1)[o]);
-                        const float sg = fast_sigmoid(a);
-                        ((bf16_t*)g.C0)[o] = f32_to_bf16(dh * b * sg * (1.0f + a * (1.0f - sg)));
-                        ((bf16_t*)g.C1)[o] = f32_to_bf16(dh * a * sg);
-                    }
-                }
-            } else if (MODE == GG_WGRAD_DOWN) {
-                const int64_t base = (int64_t)e * f * d;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = n0 + wn * 128 + j * 32 + cl;
-                    ((bf16_t*)g.C0)[base + (int64_t)(m0 + rl) * d + col] = f32_to_bf16(acc[i][j][r]);
-                }
-            } else {  // GG_WGRAD_GATEUP
-                const int64_t base = (int64_t)e * d * f;
-                const bool first = n0 < f;
-                bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
-                const int c0 = first ? n0 : n0 - f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = c0 + wn * 128 + j * 32 + cl;
-                    out[base + (int64_t)(m0 + rl) * f + col] = f32_to_bf16(acc[i][j][r]);
+                } else if (MODE == GG_WGRAD_DOWN) {
+                    const int64_t o = (int64_t)e * f * d + (int64_t)(m0 + rt) * d + n0 + ct;
+                    *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(v);
+                } else {  // GG_WGRAD_GATEUP
+                    const bool first = n0 < f;
+                    bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
+                    const int64_t o = (int64_t)e * d * f + (int64_t)(m0 + rt) * f +
+                                      (first ? n0 : n0 - f) + ct;
+                    *(u32x4*)(out + o) = Vec16<bf16_t>::pack(v);
                 }
             }
         }
