@@ -288,6 +288,23 @@ def ffn_rows_bwd_data(a_s, b_s, d_o_rows, wg, wu, wd, storage: str):
     return da, db, dxp
 
 
+def ffn_cols_fwd(xp_rows, wg, wu, cols, storage: str):
+    """Columns `cols` of a, b, h for the rows of one expert (the stored values)."""
+    xr = _f64(xp_rows)
+    a = xr @ _f64(np.asarray(wg)[:, cols])
+    b = xr @ _f64(np.asarray(wu)[:, cols])
+    h = silu(a) * b
+    return store(a, storage), store(b, storage), store(h, storage)
+
+
+def ffn_cols_bwd(a_cols, b_cols, d_o_rows, wd, cols, storage: str):
+    """Columns `cols` of da, db for the rows of one expert, from the stored a, b."""
+    dh = _f64(d_o_rows) @ _f64(np.asarray(wd)[cols, :]).T
+    a = _f64(a_cols); b = _f64(b_cols)
+    sg = sigmoid(a)
+    return store(dh * b * sg * (1.0 + a * (1.0 - sg)), storage), store(dh * a * sg, storage)
+
+
 def expert_ffn_bwd(xp, a, b, h, w_gate, w_up, w_down, offsets, d_o, storage: str):
     """B2..B5: dgrad through down, SwiGLU backward, wgrads, dgrad through gate/up."""
     n = int(offsets[-1])

@@ -62,6 +62,12 @@ CASES = {
     "valu_odd": _shape("valu_odd", T=96, d=136, E=3, K=2, f=200, sub_seq=32, cf=1.0, seed=13),
     # shared expert with a sigmoid gate
     "shared": _shape("shared", T=512, d=256, E=8, K=2, f=256, fs=512, seed=14, w_std=0.05),
+    # 64 experts plus the shared gate: the gate logit is column 64 (past the last lane)
+    "shared_e64": _shape("shared_e64", T=256, d=256, E=64, K=8, f=256, fs=256, seed=19,
+                         w_std=0.05),
+    # the same on the vector-ALU router (d not a multiple of 128)
+    "shared_e64_valu": _shape("shared_e64_valu", T=128, d=200, E=64, K=4, f=136, fs=72, sub_seq=128,
+                              seed=20, w_std=0.05),
     # one expert, top-1: a dense SwiGLU MLP
     "dense": _shape("dense", T=300, d=256, E=1, K=1, f=512, sub_seq=300, seed=15),
 }

@@ -424,3 +424,29 @@ def test_round_bf16_ties_to_even():
     vals = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20])
     out = oracle.round_bf16(vals)
     assert list(out) == [1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7]
+
+
+def test_column_restricted_ffn_equals_full():
+    """The column versions used for sampled weight-gradient checks agree with the full
+    (pinned) forward and backward."""
+    rng = np.random.default_rng(16)
+    T, d, E, K, f = 40, 12, 3, 2, 10
+    inp = _tiny_inputs(rng, T, d, E, f)
+    for k in list(inp):
+        if inp[k] is not None:
+            inp[k] = oracle.round_bf16(inp[k])
+    res = oracle.layer_fwd_bwd(inp, K, T, -1, "bf16")
+    r = res["routing"]
+    cols = np.array([0, 3, 7, 9])
+    for e in range(E):
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        a, b, h = oracle.ffn_cols_fwd(res["xp"][lo:hi], inp["w_gate"][e], inp["w_up"][e], cols,
+                                      "bf16")
+        assert np.array_equal(a, res["a"][lo:hi][:, cols])
+        assert np.array_equal(b, res["b"][lo:hi][:, cols])
+        assert np.array_equal(h, res["h"][lo:hi][:, cols])
+        da, db = oracle.ffn_cols_bwd(a, b, res["d_o"][lo:hi], inp["w_down"][e], cols, "bf16")
+        dwg = oracle.round_bf16(res["xp"][lo:hi].T @ da)
+        assert np.max(np.abs(dwg - res["dw_gate"][e][:, cols])) <= 1e-2 * np.max(np.abs(dwg))
+        dwd = oracle.round_bf16(h.T @ res["d_o"][lo:hi])
+        assert np.max(np.abs(dwd - res["dw_down"][e][cols, :])) <= 1e-2 * np.max(np.abs(dwd))

@@ -179,12 +179,14 @@ __global__ void __launch_bounds__(256) router_fwd_mfma(
         int t = t0 + tl;
         if (t >= T) break;
         float l = 0.f;
-        if (lane < E + has_sg) {
+        if (lane < E) {
             l = ((part[0][tl][lane] + part[1][tl][lane]) + part[2][tl][lane]) + part[3][tl][lane];
-            if (lane < E && bias) l = l + bias[lane];
-            if (lane < E) logits[(int64_t)t * E + lane] = l;
-            else sg_logit[t] = l;
+            if (bias) l = l + bias[lane];
+            logits[(int64_t)t * E + lane] = l;
         }
+        // the shared gate is column E, which can be past the last lane (E = 64)
+        if (has_sg && lane == 0)
+            sg_logit[t] = ((part[0][tl][E] + part[1][tl][E]) + part[2][tl][E]) + part[3][tl][E];
         softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
     }
 }
@@ -211,12 +213,12 @@ __global__ void __launch_bounds__(64) router_fwd_valu(
     }
     __syncthreads();
     float l = 0.f;
-    if (lane < ncol) {
+    if (lane < E) {
         l = lg[lane];
-        if (lane < E && bias) l = l + bias[lane];
-        if (lane < E) logits[t * E + lane] = l;
-        else sg_logit[t] = l;
+        if (bias) l = l + bias[lane];
+        logits[t * E + lane] = l;
     }
+    if (w_sg && lane == 0) sg_logit[t] = lg[E];  // column E can be past the last lane
     softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
 }
 
