@@ -15,12 +15,13 @@
 //   WGRAD_DOWN   dW_d,e = h_e^T d_o,e                  (K = the segment's rows)
 //   WGRAD_GATEUP dW_g,e = xp_e^T da_e, dW_u,e = xp_e^T db_e
 //
-// Tiling.  256 x 256 output tile, k-step 32, 256 threads = 4 waves in a 2 x 2 grid,
-// each wave 128 x 128 = 4 x 4 v_mfma_f32_32x32x16_bf16 tiles (256 fp32 accumulators
-// per lane in AGPRs, one wave per SIMD).
+// Tiling.  256 x 256 output tile, k-step 32, 512 threads = 8 waves; wave w computes
+// rows 128*(w & 1) .. +127 and columns 64*(w >> 1) .. +63 of the tile as 4 x 2
+// v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane, two waves per SIMD).
 //
-// Data path.  Operand tiles go from global memory straight into LDS with
-// global_load_lds_dwordx4 (no register staging, no LDS store instructions), in a
+// Data path.  Operand tiles go from global memory straight into LDS with direct
+// buffer loads (buffer_load_dwordx4 ... lds: no register staging, no LDS store
+// instructions, 32-bit per-lane offsets against a per-tile buffer resource), in a
 // 4-stage ring of 32 KB stages (128 KB), three k-steps in flight.  An operand whose
 // contiguous dimension is K sits in LDS as [256 rows][32 k] and a fragment is one
 // ds_read_b128; an operand whose contiguous dimension is M or N sits as it is in
@@ -31,10 +32,13 @@
 // applied by choosing which global chunk each lane fetches, since a direct load
 // writes its 64 lanes' 16 bytes to 1 KB of consecutive LDS.
 //
-// Schedule per k-step: read the fragments of sub-step 1, issue the 16 MFMAs of
-// sub-step 0, wait for the next stage and pass the barrier, refill the freed stage,
-// read the fragments of the next stage's sub-step 0, issue the 16 MFMAs of sub-step 1.
-// MFMAs already issued keep the matrix pipe busy while the wave waits at the barrier.
+// Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
+// the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
+// compute phase C(k): the 16 MFMAs of k-step k with this wave's four direct loads of
+// k-step k+3 between them -- one phase apart, separated by block barriers, so that on
+// every SIMD one wave issues MFMAs while the other reads LDS.  The LDS reads of one
+// phase take about as long as its MFMAs, and the direct loads are issued by the
+// computing wave, where their issue cost hides under the MFMA pipeline.
 //
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
 // that each XCD runs a contiguous range, in which consecutive tiles share their
@@ -148,17 +152,42 @@ template <int MODE> struct Traits {
     static constexpr bool b_mn = MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || a_mn;
 };
 
+// Buffer resource over the raw byte range [base, base + bytes): a direct load through it
+// takes a 32-bit per-lane offset (half the address traffic of a 64-bit flat address), and
+// the hardware returns zeros for offsets at or past `bytes`, which the weight-gradient
+// passes use for the k rows past the end of a segment.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc(uint64_t base, uint32_t bytes) {
+    i32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;  // raw buffer, 32-bit data format
+    return r;
+}
+__device__ __forceinline__ void lds_dma16_buf(const i32x4_t& rsrc, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(lds_addr) : "memory", "m0");
+}
+
+// One 256-thread group of four waves computes while the other loads; a SIMD runs one
+// wave of each group.  Block barriers alternate the two roles.
+constexpr int NTHREADS = 512;
+
 template <int MODE>
-__global__ void __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 gg_mfma_kernel(GemmArgs g, int total_tiles) {
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
     using TR = Traits<MODE>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wv >> 2;   // waves w and w + 4 share a SIMD and sit in different groups
+    const int wq = wv & 3;     // wave within its group
+    const int wm = wv & 1;     // output rows wm*128 .. +127 of the tile
+    const int wn = wv >> 1;    // output columns wn*64 .. +63 (gate/up: features wn*32 .. +31)
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     if (L >= total_tiles) return;
 
@@ -195,242 +224,236 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     const bf16_t* B1 = (const bf16_t*)g.B1;
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-    // ---- per-lane source offsets (elements) of this wave's 4 direct loads per operand --
-    // K-major: instruction i covers tile rows (wave*4+i)*16 + lane/4, physical chunk lane%4.
-    // MN-major: instruction i covers k rows (wave*4+i)*2 + lane/32, physical chunk lane%32.
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
-    int64_t a_off[4], b_off[4];
-    int a_kr[4], b_kr[4];
-    bool b_up[4];  // gate/up: this lane's chunk comes from W_u
+    // ---- this wave's share of the direct loads: group 0 fills the A tile of every
+    // stage, group 1 the B tile; wave wq of a group issues instructions 4wq .. 4wq+3 of
+    // the 16 that cover one 16 KB operand tile.
+    // K-major: instruction ii covers tile rows ii*16 + lane/4, physical chunk lane%4.
+    // MN-major: instruction ii covers k rows ii*2 + lane/32, physical chunk lane%32.
+    // Every operand is read through a buffer resource whose base moves with the k-step
+    // (kbase0 + kt * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed
+    // per-lane byte offset.  The gate/up forward B tile mixes W_g and W_u chunks within
+    // one instruction and keeps flat 64-bit addresses.
+    const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
+    const bool flat = MODE == GG_FWD_GATEUP && grp == 1;
+    const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
+    // row pitch (elements) of this wave's operand
+    const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
+                     : (MODE == GG_DGRAD_DOWN || MODE == GG_FWD_DOWN || MODE == GG_WGRAD_DOWN) ? d : f;
+    uint64_t kbase0, kbase1 = 0;
+    if (grp == 0) {
+        if (TR::a_mn) kbase0 = (uint64_t)(A0 + (int64_t)k_lo * ld);
+        else kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld), kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
+    } else if (MODE == GG_FWD_DOWN) {
+        kbase0 = (uint64_t)(B0 + (int64_t)e * f * d);
+    } else if (MODE == GG_DGRAD_DOWN) {
+        kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
+    } else if (MODE == GG_DGRAD_GATEUP) {
+        kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
+        kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
+    } else if (MODE == GG_WGRAD_DOWN) {
+        kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d);
+    } else if (MODE == GG_WGRAD_GATEUP) {
+        kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f);
+    } else {
+        kbase0 = 0;  // gate/up forward B: flat addresses
+    }
+    const uint64_t kstride = mn ? (uint64_t)BK * ld * 2 : (uint64_t)BK * 2;
+    const int ksplit = MODE == GG_DGRAD_GATEUP ? f / BK : nk;
+    uint32_t voff[4];
+    int64_t gofs[4];   // gate/up forward B: element offset within W_g / W_u at k-step 0
+    bool src_up[4];    // gate/up forward B: this lane's chunk comes from W_u
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        b_up[i] = false;
-        if (!TR::a_mn) {
-            const int row = (wv * 4 + i) * 16 + (lane >> 2);
+    for (int u = 0; u < 4; ++u) {
+        const int ii = wq * 4 + u;
+        src_up[u] = false;
+        gofs[u] = 0;
+        if (!mn) {
+            const int row = ii * 16 + (lane >> 2);
             const int c = (lane & 3) ^ swz_k(row);
-            const int grow = min(m0 + row, m_lim - 1);  // rows past the segment: any valid row
-            const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
-            a_off[i] = (int64_t)grow * lda + c * 8;
-            a_kr[i] = 0;
+            // A: rows past the segment read any valid row (their results are not stored)
+            const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
+            voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
         } else {
-            const int kr = (wv * 4 + i) * 2 + (lane >> 5);
+            const int kr = ii * 2 + (lane >> 5);
             const int c = (lane & 31) ^ swz_mn(kr);
-            a_off[i] = m0 + c * 8;
-            a_kr[i] = kr;
-        }
-        if (!TR::b_mn) {
-            const int row = (wv * 4 + i) * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ swz_k(row);
-            b_off[i] = MODE == GG_DGRAD_DOWN
-                           ? (int64_t)e * f * d + (int64_t)(n0 + row) * d + c * 8
-                           : (int64_t)e * d * f + (int64_t)(n0 + row) * f + c * 8;
-            b_kr[i] = 0;
-        } else {
-            const int kr = (wv * 4 + i) * 2 + (lane >> 5);
-            const int c = (lane & 31) ^ swz_mn(kr);
-            b_kr[i] = kr;
-            if (MODE == GG_FWD_GATEUP) {
-                b_up[i] = c >= 16;
-                b_off[i] = (int64_t)e * d * f + n0 + (c & 15) * 8;
-            } else if (MODE == GG_FWD_DOWN) {
-                b_off[i] = (int64_t)e * f * d + n0 + c * 8;
-            } else if (MODE == GG_WGRAD_DOWN) {
-                b_off[i] = n0 + c * 8;
+            const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
+            if (flat) {
+                src_up[u] = c >= 16;
+                gofs[u] = (int64_t)e * d * f + (int64_t)kr * f + n0 + (c & 15) * 8;
+                voff[u] = 0;
             } else {
-                b_off[i] = (n0 < f ? n0 : n0 - f) + c * 8;
+                voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
             }
         }
     }
 
-    // Issue the i-th direct load of each operand of k-step kt into stage st.
-    auto issue_one = [&](int kt, int st, int i) {
-        const uint32_t sa = smem_base + st * STAGE_BYTES + wv * 4 * 1024;
-        const uint32_t sb = sa + TILE_BYTES;
-        const int k0 = kt * BK;
-        const bool first_half = k0 < f;            // gate/up dgrad: da, W_g then db, W_u
-        const int kh = first_half ? k0 : k0 - f;
-        {
-            const bf16_t* pa;
-            const bf16_t* pb;
-            if (MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || MODE == GG_DGRAD_DOWN) {
-                pa = A0 + a_off[i] + k0;
-            } else if (MODE == GG_DGRAD_GATEUP) {
-                pa = (first_half ? A0 : A1) + a_off[i] + kh;
-            } else {
-                const int kr = min(k_lo + k0 + a_kr[i], k_hi - 1);  // tail rows zeroed later
-                pa = A0 + a_off[i] + (int64_t)kr * (MODE == GG_WGRAD_DOWN ? f : d);
+    // Issue the u-th of this wave's four direct loads of k-step kt into stage st.
+    auto issue_one = [&](int kt, int st, int u) {
+        const uint32_t dst = smem_base + st * STAGE_BYTES + grp * TILE_BYTES + wq * 4 * 1024 + u * 1024;
+        if (flat) {
+            const bf16_t* p = (src_up[u] ? B1 : B0) + gofs[u] + (int64_t)kt * BK * f;
+            lds_dma16(p, dst);
+        } else {
+            const bool second = kt >= ksplit;
+            const uint64_t base = (second ? kbase1 : kbase0) +
+                                  (uint64_t)(second ? kt - ksplit : kt) * kstride;
+            uint32_t bytes = 0xFFFFFFF0u;
+            if (TR::a_mn) {
+                // weight gradients: k rows past the segment read as zeros
+                const int64_t rows_left = (int64_t)(k_hi - k_lo) - (int64_t)kt * BK;
+                const int64_t nb = rows_left * ld * 2;
+                bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
             }
-            if (MODE == GG_DGRAD_DOWN) {
-                pb = B0 + b_off[i] + k0;
-            } else if (MODE == GG_DGRAD_GATEUP) {
-                pb = (first_half ? B0 : B1) + b_off[i] + kh;
-            } else if (MODE == GG_FWD_GATEUP) {
-                pb = (b_up[i] ? B1 : B0) + b_off[i] + (int64_t)(k0 + b_kr[i]) * f;
-            } else if (MODE == GG_FWD_DOWN) {
-                pb = B0 + b_off[i] + (int64_t)(k0 + b_kr[i]) * d;
-            } else {
-                const int kr = min(k_lo + k0 + b_kr[i], k_hi - 1);
-                pb = (MODE == GG_WGRAD_GATEUP && n0 >= f ? B1 : B0) + b_off[i] +
-                     (int64_t)kr * (MODE == GG_WGRAD_DOWN ? d : f);
-            }
-            lds_dma16(pa, sa + i * 1024);
-            lds_dma16(pb, sb + i * 1024);
+            lds_dma16_buf(make_rsrc(base, bytes), voff[u], dst);
         }
     };
     auto issue = [&](int kt, int st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) issue_one(kt, st, i);
+        for (int u = 0; u < 4; ++u) issue_one(kt, st, u);
     };
 
-    // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads.
-    uint32_t a_rd[2][4], b_rd[2][4];
+    // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads:
+    // 4 A fragments (32 rows each) and 2 B fragments (32 columns each) per sub-step.
+    uint32_t a_rd[2][4], b_rd[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
             a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
                                    : addr_k(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
-            // gate/up: gate columns are tile rows 0..127, up columns 128..255
-            const int c0 = MODE == GG_FWD_GATEUP
-                               ? (i < 2 ? wn * 64 + i * 32 : 128 + wn * 64 + (i - 2) * 32)
-                               : wn * 128 + i * 32;
-            b_rd[ks][i] = TR::b_mn ? addr_mn(TILE_BYTES, c0, ks, lane)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            // gate/up: gate columns are tile rows 0..127 of B, up columns 128..255
+            const int c0 = MODE == GG_FWD_GATEUP ? j * 128 + wn * 32 : wn * 64 + j * 32;
+            b_rd[ks][j] = TR::b_mn ? addr_mn(TILE_BYTES, c0, ks, lane)
                                    : addr_k(TILE_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
         }
     }
-    // The r-th read of a sub-step's fragments: A fragments first, then B.
-    auto read_op = [&](int r, uint32_t stage, int ks, Frag& fa, Frag& fb) {
-        if (TR::a_mn) {
-            if (r < 4) ds_tr_pair(fa.lo[r], fa.hi[r], stage + a_rd[ks][r]);
-        } else {
-            if (r < 4) ds_b128(fa.q[r], stage + a_rd[ks][r]);
-        }
-        if (r >= 4 && r < 8) {
-            const int j = r - 4;
-            if (TR::b_mn) ds_tr_pair(fb.lo[j], fb.hi[j], stage + b_rd[ks][j]);
-            else ds_b128(fb.q[j], stage + b_rd[ks][j]);
+
+    Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
+    auto read_stage = [&](uint32_t stage) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], stage + a_rd[ks][i]);
+                else ds_b128(fa[ks].q[i], stage + a_rd[ks][i]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
+                else ds_b128(fb[ks].q[j], stage + b_rd[ks][j]);
+            }
         }
     };
 
-    // Rows [valid, 32) of the A tile of stage st hold clamped copies: zero them (wgrad K tail).
-    auto zero_tail = [&](int st, int valid) {
-        const uint32_t ta = smem_base + st * STAGE_BYTES;
-        for (int idx = tid; idx < (BK - valid) * 32; idx += 256) {
-            const int r = valid + idx / 32, c = idx % 32;
-            *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)(ta + r * 512 + c * 16) =
-                u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
-
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int tail_valid = TR::a_mn ? (k_hi - k_lo) - (nk - 1) * BK : BK;
+    // Wait until this wave's loads of k-step kt+1 have landed, leaving the loads of
+    // the `ahead` later k-steps that exist in flight.
+    auto wait_next = [&](int kt, int ahead) {
+        if (kt + 1 >= nk) return;
+        const int newer = min(ahead, nk - 2 - kt);
+        if (newer >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (newer == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    };
 
+    // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
+    // the 16 MFMAs of k-step k, with this wave's four loads of k-step k+3 (into the stage
+    // k-step k-1 used, which both groups have read by then) between them.  Group 0 runs
+    // M(0) C(0) M(1) C(1) ..., group 1 the same one phase later, with a block barrier
+    // between phases: while one wave of a SIMD issues MFMAs, the other reads LDS.
+    // Before the barrier that opens M(k+1) of group 0, each wave has waited for its own
+    // loads of k-step k+1: group 0 at the end of C(k) (k-steps k+2, k+3 may be in
+    // flight), group 1 at the end of M(k) (k+2 may be).  Every wave passes 2 nk + 2
+    // barriers.
     if (nk > 0) {
-        Frag f0a, f0b, f1a, f1b;  // sub-step 0 and sub-step 1 fragments
         issue(0, 0);
         if (nk > 1) issue(1, 1);
         if (nk > 2) issue(2, 2);
-        if (nk > 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else if (nk > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        if (nk > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_barrier();
-        if (TR::a_mn && nk == 1 && tail_valid < BK) {
-            zero_tail(0, tail_valid);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) read_op(r, smem_base, 0, f0a, f0b);
+        if (grp == 1) __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
 
         for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt & (STAGES - 1);
-            const uint32_t stage = smem_base + st * STAGE_BYTES;
-            const bool more = kt + 1 < nk;
-            const uint32_t next = smem_base + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES;
-
-            // Phase A: MFMAs of sub-step 0, with the reads of sub-step 1 between them.
-            // One MFMA and one read per slot, fenced so the compiler keeps the order.
+            // ---- memory phase
+            read_stage(smem_base + (kt & (STAGES - 1)) * STAGE_BYTES);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (grp == 1) wait_next(kt, 1);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- compute phase
+            __builtin_amdgcn_s_setprio(1);
+            const bool refill = kt + 3 < nk;
+            const int st3 = (kt + 3) & (STAGES - 1);
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int i = q >> 2, j = q & 3;
+                const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    frag_value<TR::a_mn>(f0a, i), frag_value<TR::b_mn>(f0b, j), acc[i][j], 0, 0, 0);
-                if (q < 8) read_op(q, stage, 1, f1a, f1b);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (more) {
-                // the loads of k-step kt+1 have landed in this wave; after the barrier, in all
-                if (kt + 2 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                __builtin_amdgcn_s_barrier();
-                if (TR::a_mn && kt + 2 == nk && tail_valid < BK) {
-                    zero_tail((kt + 1) & (STAGES - 1), tail_valid);
-                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    __builtin_amdgcn_s_barrier();
+                    frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
+                    acc[i][j], 0, 0, 0);
+                if ((q & 3) == 1 && refill) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    issue_one(kt + 3, st3, q >> 2);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // Phase B: MFMAs of sub-step 1, with the reads of the next stage's sub-step 0
-            // and the refill of the stage freed by the previous k-step between them.  After
-            // the last k-step the reads touch a stage nobody uses: in bounds, and unused.
+            __builtin_amdgcn_s_setprio(0);
+            if (grp == 0) wait_next(kt, 2);
             __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int i = q >> 2, j = q & 3;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    frag_value<TR::a_mn>(f1a, i), frag_value<TR::b_mn>(f1b, j), acc[i][j], 0, 0, 0);
-                if (q < 8) read_op(q, next, 0, f0a, f0b);
-                else if (q < 12 && kt + 3 < nk) issue_one(kt + 3, (kt + 3) & (STAGES - 1), q - 8);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (grp == 0) __builtin_amdgcn_s_barrier();
     }
 
     // Epilogue.  32x32 MFMA result: lane holds column (lane & 31) and rows
     // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r.  Each wave stages one
-    // 32-row band of its fp32 results at a time in a private 32 KB of LDS, then every
-    // lane handles 8-column chunks: 16-byte coalesced loads of epilogue inputs and
-    // 16-byte stores (16 lanes cover 256 contiguous bytes of a row).
-    __builtin_amdgcn_s_barrier();  // every wave is done reading the operand stages
+    // 32-row band of its fp32 results (32 x 64) at a time in a private 8.5 KB of LDS,
+    // then every lane handles 8-column chunks: 16-byte loads of epilogue inputs and
+    // 16-byte stores.  Every wave has passed the last barrier after the last reads of
+    // the operand stages, and no direct load is in flight.
     typedef __attribute__((address_space(3))) float lds_f32;
-    const uint32_t wbase = smem_base + wv * 32768;
+    typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+    constexpr int P = 68;  // band row pitch in floats
+    const uint32_t wbase = smem_base + wv * (32 * P * 4);
     const int cl = lane & 31;
     const int rq = 4 * (lane >> 5);
-    constexpr int P = MODE == GG_FWD_GATEUP ? 68 : 132;  // band row pitch in floats
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // gate/up: columns j = 0, 1 are a (first buffer), j = 2, 3 are b (second)
-            const uint32_t buf = (MODE == GG_FWD_GATEUP && j >= 2) ? wbase + 32 * P * 4 : wbase;
-            const int col = (MODE == GG_FWD_GATEUP ? (j & 1) : j) * 32 + cl;
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rl = 8 * (r >> 2) + rq + (r & 3);
-                *(lds_f32*)(uintptr_t)(buf + (rl * P + col) * 4) = acc[i][j][r];
+                *(lds_f32*)(uintptr_t)(wbase + (rl * P + j * 32 + cl) * 4) = acc[i][j][r];
             }
-        }
         const int row_base = wm * 128 + i * 32;  // within the block tile
         if (MODE == GG_FWD_GATEUP) {
+            // band columns 0..31: a of features wn*32 + 0..31; columns 32..63: b of the same
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < 2; ++t) {
                 const int q = lane + 64 * t;
-                const int rl = q >> 3, cc = q & 7;
+                const int rl = q >> 2, cc = q & 3;
                 const int row = m0 + row_base + rl;
                 const uint32_t la = wbase + (rl * P + cc * 8) * 4;
-                const uint32_t lb = la + 32 * P * 4;
-                u32x4_t a0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)la;
-                u32x4_t a1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(la + 16);
-                u32x4_t b0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)lb;
-                u32x4_t b1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(lb + 16);
+                const uint32_t lb = la + 32 * 4;
+                u32x4_t a0 = *(const lds_u32x4*)(uintptr_t)la;
+                u32x4_t a1 = *(const lds_u32x4*)(uintptr_t)(la + 16);
+                u32x4_t b0 = *(const lds_u32x4*)(uintptr_t)lb;
+                u32x4_t b1 = *(const lds_u32x4*)(uintptr_t)(lb + 16);
                 if (row < m_lim) {
                     float av[8], bv[8], hv[8];
 #pragma unroll
@@ -440,7 +463,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                     }
 #pragma unroll
                     for (int u = 0; u < 8; ++u) hv[u] = av[u] * fast_sigmoid(av[u]) * bv[u];
-                    const int64_t o = (int64_t)row * f + n0 + wn * 64 + cc * 8;
+                    const int64_t o = (int64_t)row * f + n0 + wn * 32 + cc * 8;
                     *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(av);
                     *(u32x4*)((bf16_t*)g.C1 + o) = Vec16<bf16_t>::pack(bv);
                     *(u32x4*)((bf16_t*)g.C2 + o) = Vec16<bf16_t>::pack(hv);
@@ -448,17 +471,17 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             }
         } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 4; ++t) {
                 const int q = lane + 64 * t;
-                const int rl = q >> 4, cc = q & 15;
+                const int rl = q >> 3, cc = q & 7;
                 const uint32_t la = wbase + (rl * P + cc * 8) * 4;
-                u32x4_t v0 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)la;
-                u32x4_t v1 = *(const __attribute__((address_space(3))) u32x4_t*)(uintptr_t)(la + 16);
+                u32x4_t v0 = *(const lds_u32x4*)(uintptr_t)la;
+                u32x4_t v1 = *(const lds_u32x4*)(uintptr_t)(la + 16);
                 float v[8];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) { v[u] = __uint_as_float(v0[u]); v[u + 4] = __uint_as_float(v1[u]); }
                 const int rt = row_base + rl;              // row within the block tile
-                const int ct = wn * 128 + cc * 8;          // column within the block tile
+                const int ct = wn * 64 + cc * 8;           // column within the block tile
                 if (MODE == GG_FWD_DOWN || MODE == GG_DGRAD_GATEUP) {
                     const int row = m0 + rt;
                     if (row < m_lim)
@@ -496,7 +519,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
 
 template <int MODE>
 hipError_t launch_mode(const GemmArgs& a, unsigned g8, int total, hipStream_t s) {
-    gg_mfma_kernel<MODE><<<g8, 256, 0, s>>>(a, total);
+    gg_mfma_kernel<MODE><<<g8, NTHREADS, 0, s>>>(a, total);
     return hipGetLastError();
 }
 
