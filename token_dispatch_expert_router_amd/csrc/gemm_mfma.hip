@@ -94,16 +94,6 @@ __device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ o
 __device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int swz_mn(int r) { return (r & 3) << 2; }
 
-// Direct global -> LDS load of 16 bytes per lane (the 64 lanes fill 1 KB of LDS
-// starting at lds_addr, which must be wave-uniform).  Written as inline asm so that
-// the compiler does not treat every later LDS read as possibly aliasing it (it would
-// wait for all loads in flight before each read); completion is awaited explicitly
-// with s_waitcnt vmcnt before the barrier that publishes a stage.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds_addr) : "memory", "m0");
-}
-
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
 
@@ -131,6 +121,21 @@ __device__ __forceinline__ uint32_t addr_mn(uint32_t tile, int c0, int ks, int l
     return tile + kr * 512 + (((col >> 3) ^ swz_mn(kr)) << 4) + (col & 7) * 2;
 }
 
+// Gate/up forward B tile: two sub-tiles [32 k][128 cols] (W_g columns, then W_u), 256-byte
+// k rows, physical chunk = logical chunk ^ 4*(k & 3).  A 32-lane half of a transpose
+// read covers 4 consecutive k rows x 64 bytes, which this swizzle spreads over all 64
+// banks.  The second read of a fragment is 4 k rows (1024 bytes) further.
+__device__ __forceinline__ uint32_t addr_mn_split(uint32_t sub, int c0, int ks, int lane) {
+    const int g = lane >> 4, s = lane & 15;
+    const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
+    const int kr = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    return sub + kr * 256 + (((col >> 3) ^ (4 * (kr & 3))) << 4) + (col & 7) * 2;
+}
+__device__ __forceinline__ void ds_tr_pair_1k(s16x4_t& lo, s16x4_t& hi, uint32_t addr) {
+    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
+    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + 1024));
+}
+
 struct Frag {
     s16x4_t lo[4], hi[4];  // MN-major fragments (two transpose reads)
     u32x4_t q[4];          // K-major fragments (one read)
@@ -156,6 +161,12 @@ template <int MODE> struct Traits {
 // takes a 32-bit per-lane offset (half the address traffic of a 64-bit flat address), and
 // the hardware returns zeros for offsets at or past `bytes`, which the weight-gradient
 // passes use for the k rows past the end of a segment.
+//
+// The direct load (16 bytes per lane; the 64 lanes fill 1 KB of LDS starting at the
+// wave-uniform address in M0) is written as inline asm so that the compiler does not
+// treat every later LDS read as possibly aliasing it (it would wait for all loads in
+// flight before each read); completion is awaited explicitly with s_waitcnt vmcnt
+// before the barrier that publishes a stage.  The asm has no register outputs.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4_t make_rsrc(uint64_t base, uint32_t bytes) {
     i32x4_t r;
@@ -229,12 +240,12 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     // the 16 that cover one 16 KB operand tile.
     // K-major: instruction ii covers tile rows ii*16 + lane/4, physical chunk lane%4.
     // MN-major: instruction ii covers k rows ii*2 + lane/32, physical chunk lane%32.
+    // Gate/up forward B: instruction ii covers k rows 4*(ii%8) + lane/16 of sub-tile ii/8
+    // (W_g, then W_u), physical chunk lane%16.
     // Every operand is read through a buffer resource whose base moves with the k-step
     // (kbase0 + kt * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed
-    // per-lane byte offset.  The gate/up forward B tile mixes W_g and W_u chunks within
-    // one instruction and keeps flat 64-bit addresses.
+    // per-lane byte offset.
     const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
-    const bool flat = MODE == GG_FWD_GATEUP && grp == 1;
     const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
     // row pitch (elements) of this wave's operand
     const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
@@ -254,20 +265,20 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d);
     } else if (MODE == GG_WGRAD_GATEUP) {
         kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f);
-    } else {
-        kbase0 = 0;  // gate/up forward B: flat addresses
+    } else {  // gate/up forward B: waves 0-1 of the group load W_g, waves 2-3 W_u
+        kbase0 = (uint64_t)((wq >= 2 ? B1 : B0) + (int64_t)e * d * f + n0);
     }
     const uint64_t kstride = mn ? (uint64_t)BK * ld * 2 : (uint64_t)BK * 2;
     const int ksplit = MODE == GG_DGRAD_GATEUP ? f / BK : nk;
     uint32_t voff[4];
-    int64_t gofs[4];   // gate/up forward B: element offset within W_g / W_u at k-step 0
-    bool src_up[4];    // gate/up forward B: this lane's chunk comes from W_u
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int ii = wq * 4 + u;
-        src_up[u] = false;
-        gofs[u] = 0;
-        if (!mn) {
+        if (MODE == GG_FWD_GATEUP && grp == 1) {
+            const int kr = 4 * (ii & 7) + (lane >> 4);
+            const int c = (lane & 15) ^ (4 * (kr & 3));
+            voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
+        } else if (!mn) {
             const int row = ii * 16 + (lane >> 2);
             const int c = (lane & 3) ^ swz_k(row);
             // A: rows past the segment read any valid row (their results are not stored)
@@ -277,23 +288,14 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             const int kr = ii * 2 + (lane >> 5);
             const int c = (lane & 31) ^ swz_mn(kr);
             const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
-            if (flat) {
-                src_up[u] = c >= 16;
-                gofs[u] = (int64_t)e * d * f + (int64_t)kr * f + n0 + (c & 15) * 8;
-                voff[u] = 0;
-            } else {
-                voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
-            }
+            voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
         }
     }
 
     // Issue the u-th of this wave's four direct loads of k-step kt into stage st.
     auto issue_one = [&](int kt, int st, int u) {
         const uint32_t dst = smem_base + st * STAGE_BYTES + grp * TILE_BYTES + wq * 4 * 1024 + u * 1024;
-        if (flat) {
-            const bf16_t* p = (src_up[u] ? B1 : B0) + gofs[u] + (int64_t)kt * BK * f;
-            lds_dma16(p, dst);
-        } else {
+        {
             const bool second = kt >= ksplit;
             const uint64_t base = (second ? kbase1 : kbase0) +
                                   (uint64_t)(second ? kt - ksplit : kt) * kstride;
@@ -323,9 +325,10 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                                    : addr_k(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            // gate/up: gate columns are tile rows 0..127 of B, up columns 128..255
-            const int c0 = MODE == GG_FWD_GATEUP ? j * 128 + wn * 32 : wn * 64 + j * 32;
-            b_rd[ks][j] = TR::b_mn ? addr_mn(TILE_BYTES, c0, ks, lane)
+            // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
+            const int c0 = wn * 64 + j * 32;
+            b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(TILE_BYTES + j * 8192, wn * 32, ks, lane)
+                        : TR::b_mn ? addr_mn(TILE_BYTES, c0, ks, lane)
                                    : addr_k(TILE_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
         }
     }
@@ -341,7 +344,8 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
+                if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
+                else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
                 else ds_b128(fb[ks].q[j], stage + b_rd[ks][j]);
             }
         }
