@@ -21,21 +21,26 @@
 //
 // Data path.  Operand tiles go from global memory straight into LDS with direct
 // buffer loads (buffer_load_dwordx4 ... lds: no register staging, no LDS store
-// instructions, 32-bit per-lane offsets against a per-tile buffer resource), in a
-// 4-stage ring of 32 KB stages (128 KB), three k-steps in flight.  An operand whose
-// contiguous dimension is K sits in LDS as [256 rows][32 k] and a fragment is one
+// instructions, 32-bit per-lane offsets against a per-tile buffer resource).  An operand
+// whose contiguous dimension is K sits in LDS as [256 rows][k] and a fragment is one
 // ds_read_b128; an operand whose contiguous dimension is M or N sits as it is in
 // memory, [32 k][256 cols], and a fragment is two ds_read_b64_tr_b16 (the LDS
 // transpose read of gfx950: in each 16-lane group, lane i receives element i%4 of the
-// 8 bytes addressed by lane 4j + i/4, for j = 0..3).  Both layouts XOR-swizzle their
+// 8 bytes addressed by lane 4j + i/4, for j = 0..3).  All layouts XOR-swizzle their
 // 16-byte chunks so that the fragment reads are free of bank conflicts; the swizzle is
 // applied by choosing which global chunk each lane fetches, since a direct load
 // writes its 64 lanes' 16 bytes to 1 KB of consecutive LDS.
 //
+// Staging.  Passes with an M- or N-major operand use a 4-stage ring of single k-steps
+// (32 KB each, three k-steps in flight).  The two dgrad passes, whose operands are both
+// K-major, load pairs of k-steps into two 64 KB slots instead, so that a K-major row
+// is 128 bytes and every load instruction reads whole cache lines (a single k-step
+// would use half of each line it touches, halving the load path's throughput).
+//
 // Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
 // the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
-// compute phase C(k): the 16 MFMAs of k-step k with this wave's four direct loads of
-// k-step k+3 between them -- one phase apart, separated by block barriers, so that on
+// compute phase C(k): the 16 MFMAs of k-step k with this wave's share of the direct
+// loads between them -- one phase apart, separated by block barriers, so that on
 // every SIMD one wave issues MFMAs while the other reads LDS.  The LDS reads of one
 // phase take about as long as its MFMAs, and the direct loads are issued by the
 // computing wave, where their issue cost hides under the MFMA pipeline.
@@ -57,9 +62,15 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 32;
-constexpr int STAGES = 4;
-constexpr int TILE_BYTES = BM * BK * 2;          // one operand tile of one stage: 16 KB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // A and B
+// Two staging schemes share the 128 KB of LDS:
+//  - single k-steps: a ring of 4 stages of 32 KB ([A 16 KB | B 16 KB] per k-step);
+//  - pairs of k-steps: 2 slots of 64 KB ([A 32 KB | B 32 KB] per 64 k).
+constexpr int STEP_STAGES = 4;
+constexpr int STEP_TILE_BYTES = BM * BK * 2;            // one operand of one k-step: 16 KB
+constexpr int STEP_STAGE_BYTES = 2 * STEP_TILE_BYTES;   // A and B of one k-step
+constexpr int KP = 2 * BK;                              // k of one pair
+constexpr int OP_BYTES = BM * KP * 2;                   // one operand of one pair: 32 KB
+constexpr int SLOT_BYTES = 2 * OP_BYTES;                // A and B of one pair: 64 KB
 
 __device__ __forceinline__ int xcd_remap(int b, int G8) {
     return (b & 7) * (G8 >> 3) + (b >> 3);
@@ -86,13 +97,16 @@ __device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ o
     return false;
 }
 
-// Swizzles.  K-major tile [256][32]: physical chunk p of row r holds logical chunk
-// p ^ swz_k(r).  MN-major tile [32][256]: physical chunk p of k-row r holds logical
-// chunk p ^ swz_mn(r).  gfx950 serves a ds_read_b128 16 consecutive lanes at a time
-// over 64 four-byte banks; with these swizzles the fragment reads of both layouts
-// measure free of bank conflicts (SQ_LDS_BANK_CONFLICT).
-__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
+// Swizzles.  K-major pair tile [256 rows][64 k] (128-byte rows): physical chunk p of
+// row r holds logical chunk p ^ ((r >> 1) & 7); a ds_read_b128 is served 16 consecutive
+// lanes (16 consecutive rows, one logical chunk) at a time over 64 four-byte banks, and
+// rows r, r+1 differ in bit 3 of the bank group while (r >> 1) & 7 spreads the eight
+// row pairs, so the 16 reads hit distinct banks.  MN-major tile [32 k][256 cols]
+// (512-byte rows): physical chunk p of k-row r holds logical chunk p ^ swz_mn(r).
 __device__ __forceinline__ int swz_mn(int r) { return (r & 3) << 2; }
+// K-major single-k-step tile [256 rows][32 k] (64-byte rows): physical chunk p of row r
+// holds logical chunk p ^ swz_k(r).
+__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -107,7 +121,7 @@ __device__ __forceinline__ void ds_tr_pair(s16x4_t& lo, s16x4_t& hi, uint32_t ad
     hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + 2048));
 }
 
-// Byte address of a K-major fragment: row of the tile, 16-byte chunk.
+// Byte address of a K-major fragment of a single-k-step tile: row of the tile, chunk.
 __device__ __forceinline__ uint32_t addr_k(uint32_t tile, int row, int chunk) {
     return tile + row * 64 + ((chunk ^ swz_k(row)) << 4);
 }
@@ -155,6 +169,10 @@ __device__ __forceinline__ float fast_sigmoid(float a) { return 1.0f / (1.0f + _
 template <int MODE> struct Traits {
     static constexpr bool a_mn = MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP;
     static constexpr bool b_mn = MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || a_mn;
+    // Both operands K-major: load pairs of k-steps so that every direct-load instruction
+    // reads whole 128-byte lines (a K-major k-step row is only 64 bytes); the other
+    // passes keep the deeper single-k-step ring.
+    static constexpr bool paired = !a_mn && !b_mn;
 };
 
 // Buffer resource over the raw byte range [base, base + bytes): a direct load through it
@@ -189,7 +207,7 @@ template <int MODE>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 gg_mfma_kernel(GemmArgs g, int total_tiles) {
-    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
     using TR = Traits<MODE>;
 
     const int tid = threadIdx.x;
@@ -235,122 +253,6 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     const bf16_t* B1 = (const bf16_t*)g.B1;
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-    // ---- this wave's share of the direct loads: group 0 fills the A tile of every
-    // stage, group 1 the B tile; wave wq of a group issues instructions 4wq .. 4wq+3 of
-    // the 16 that cover one 16 KB operand tile.
-    // K-major: instruction ii covers tile rows ii*16 + lane/4, physical chunk lane%4.
-    // MN-major: instruction ii covers k rows ii*2 + lane/32, physical chunk lane%32.
-    // Gate/up forward B: instruction ii covers k rows 4*(ii%8) + lane/16 of sub-tile ii/8
-    // (W_g, then W_u), physical chunk lane%16.
-    // Every operand is read through a buffer resource whose base moves with the k-step
-    // (kbase0 + kt * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed
-    // per-lane byte offset.
-    const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
-    const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
-    // row pitch (elements) of this wave's operand
-    const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
-                     : (MODE == GG_DGRAD_DOWN || MODE == GG_FWD_DOWN || MODE == GG_WGRAD_DOWN) ? d : f;
-    uint64_t kbase0, kbase1 = 0;
-    if (grp == 0) {
-        if (TR::a_mn) kbase0 = (uint64_t)(A0 + (int64_t)k_lo * ld);
-        else kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld), kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
-    } else if (MODE == GG_FWD_DOWN) {
-        kbase0 = (uint64_t)(B0 + (int64_t)e * f * d);
-    } else if (MODE == GG_DGRAD_DOWN) {
-        kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
-    } else if (MODE == GG_DGRAD_GATEUP) {
-        kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
-        kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
-    } else if (MODE == GG_WGRAD_DOWN) {
-        kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d);
-    } else if (MODE == GG_WGRAD_GATEUP) {
-        kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f);
-    } else {  // gate/up forward B: waves 0-1 of the group load W_g, waves 2-3 W_u
-        kbase0 = (uint64_t)((wq >= 2 ? B1 : B0) + (int64_t)e * d * f + n0);
-    }
-    const uint64_t kstride = mn ? (uint64_t)BK * ld * 2 : (uint64_t)BK * 2;
-    const int ksplit = MODE == GG_DGRAD_GATEUP ? f / BK : nk;
-    uint32_t voff[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int ii = wq * 4 + u;
-        if (MODE == GG_FWD_GATEUP && grp == 1) {
-            const int kr = 4 * (ii & 7) + (lane >> 4);
-            const int c = (lane & 15) ^ (4 * (kr & 3));
-            voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
-        } else if (!mn) {
-            const int row = ii * 16 + (lane >> 2);
-            const int c = (lane & 3) ^ swz_k(row);
-            // A: rows past the segment read any valid row (their results are not stored)
-            const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
-            voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
-        } else {
-            const int kr = ii * 2 + (lane >> 5);
-            const int c = (lane & 31) ^ swz_mn(kr);
-            const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
-            voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
-        }
-    }
-
-    // Issue the u-th of this wave's four direct loads of k-step kt into stage st.
-    auto issue_one = [&](int kt, int st, int u) {
-        const uint32_t dst = smem_base + st * STAGE_BYTES + grp * TILE_BYTES + wq * 4 * 1024 + u * 1024;
-        {
-            const bool second = kt >= ksplit;
-            const uint64_t base = (second ? kbase1 : kbase0) +
-                                  (uint64_t)(second ? kt - ksplit : kt) * kstride;
-            uint32_t bytes = 0xFFFFFFF0u;
-            if (TR::a_mn) {
-                // weight gradients: k rows past the segment read as zeros
-                const int64_t rows_left = (int64_t)(k_hi - k_lo) - (int64_t)kt * BK;
-                const int64_t nb = rows_left * ld * 2;
-                bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
-            }
-            lds_dma16_buf(make_rsrc(base, bytes), voff[u], dst);
-        }
-    };
-    auto issue = [&](int kt, int st) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) issue_one(kt, st, u);
-    };
-
-    // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads:
-    // 4 A fragments (32 rows each) and 2 B fragments (32 columns each) per sub-step.
-    uint32_t a_rd[2][4], b_rd[2][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
-                                   : addr_k(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
-            const int c0 = wn * 64 + j * 32;
-            b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(TILE_BYTES + j * 8192, wn * 32, ks, lane)
-                        : TR::b_mn ? addr_mn(TILE_BYTES, c0, ks, lane)
-                                   : addr_k(TILE_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
-        }
-    }
-
-    Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
-    auto read_stage = [&](uint32_t stage) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], stage + a_rd[ks][i]);
-                else ds_b128(fa[ks].q[i], stage + a_rd[ks][i]);
-            }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
-                else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
-                else ds_b128(fb[ks].q[j], stage + b_rd[ks][j]);
-            }
-        }
-    };
-
     f32x16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -359,68 +261,374 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Wait until this wave's loads of k-step kt+1 have landed, leaving the loads of
-    // the `ahead` later k-steps that exist in flight.
-    auto wait_next = [&](int kt, int ahead) {
-        if (kt + 1 >= nk) return;
-        const int newer = min(ahead, nk - 2 - kt);
-        if (newer >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (newer == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    };
+    if constexpr (TR::paired) {
+        // ---- direct loads.  K-steps are loaded in pairs (64 k) into two 64 KB slots
+        // [A 32 KB | B 32 KB]; group 0 loads A, group 1 loads B, and wave wq of a group issues
+        // instructions 8wq .. 8wq+7 of the 32 (1 KB each) that cover one operand of a pair.
+        //   K-major operand: [256 rows][64 k] with 128-byte rows, so that every instruction
+        //     reads whole 128-byte lines: instruction ii covers rows 8ii + lane/8, physical
+        //     chunk lane%8 (swizzle chunk ^ ((row >> 1) & 7)).
+        //   MN-major operand: two k-step tiles [32 k][256 cols] (k-step 2p at 0, 2p+1 at
+        //     16 KB); instruction ii covers tile ii/16, k rows 2(ii%16) + lane/32, physical
+        //     chunk lane%32.
+        //   Gate/up forward B: two k-step tiles, each [W_g sub-tile | W_u sub-tile];
+        //     instruction ii covers tile ii/16, sub-tile (ii/8)%2, k rows 4(ii%8) + lane/16,
+        //     physical chunk lane%16.
+        // Every load goes through a buffer resource whose base moves with the pair (kbase0 +
+        // p * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed per-lane
+        // byte offset.
+        const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
+        const int hw = wq >> 1;  // MN-major operands: the k-step of the pair this wave loads
+        const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
+        // row pitch (elements) of this wave's operand
+        const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
+                         : (MODE == GG_DGRAD_DOWN || MODE == GG_FWD_DOWN || MODE == GG_WGRAD_DOWN) ? d : f;
+        const int64_t kofs = mn ? (int64_t)hw * BK * ld : 0;  // MN-major: first k row of this wave's k-step
+        uint64_t kbase0, kbase1 = 0;
+        if (grp == 0) {
+            if (TR::a_mn) kbase0 = (uint64_t)(A0 + (int64_t)k_lo * ld + kofs);
+            else kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld), kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
+        } else if (MODE == GG_FWD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + kofs);
+        } else if (MODE == GG_DGRAD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
+        } else if (MODE == GG_DGRAD_GATEUP) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
+            kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
+        } else if (MODE == GG_WGRAD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d + kofs);
+        } else if (MODE == GG_WGRAD_GATEUP) {
+            kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f + kofs);
+        } else {  // gate/up forward B: odd waves of the group load W_u, even waves W_g
+            kbase0 = (uint64_t)(((wq & 1) ? B1 : B0) + (int64_t)e * d * f + n0 + kofs);
+        }
+        const uint64_t kstride = mn ? (uint64_t)KP * ld * 2 : (uint64_t)KP * 2;
+        const int psplit = MODE == GG_DGRAD_GATEUP ? f / KP : 0x7FFFFFFF;
+        const int np = (nk + 1) >> 1;
+        uint32_t voff[8];
+    #pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ii = wq * 8 + u;
+            const int jj = ii & 15;
+            if (MODE == GG_FWD_GATEUP && grp == 1) {
+                const int kr = 4 * (jj & 7) + (lane >> 4);
+                const int c = (lane & 15) ^ (4 * (kr & 3));
+                voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
+            } else if (!mn) {
+                const int row = ii * 8 + (lane >> 3);
+                const int c = (lane & 7) ^ ((row >> 1) & 7);
+                // A: rows past the segment read any valid row (their results are not stored)
+                const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
+                voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
+            } else {
+                const int kr = 2 * jj + (lane >> 5);
+                const int c = (lane & 31) ^ swz_mn(kr);
+                const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
+                voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
+            }
+        }
 
-    // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
-    // the 16 MFMAs of k-step k, with this wave's four loads of k-step k+3 (into the stage
-    // k-step k-1 used, which both groups have read by then) between them.  Group 0 runs
-    // M(0) C(0) M(1) C(1) ..., group 1 the same one phase later, with a block barrier
-    // between phases: while one wave of a SIMD issues MFMAs, the other reads LDS.
-    // Before the barrier that opens M(k+1) of group 0, each wave has waited for its own
-    // loads of k-step k+1: group 0 at the end of C(k) (k-steps k+2, k+3 may be in
-    // flight), group 1 at the end of M(k) (k+2 may be).  Every wave passes 2 nk + 2
-    // barriers.
-    if (nk > 0) {
-        issue(0, 0);
-        if (nk > 1) issue(1, 1);
-        if (nk > 2) issue(2, 2);
-        if (nk > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_barrier();
-        if (grp == 1) __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        // Issue the u-th of this wave's eight direct loads of pair p.
+        auto issue_one = [&](int p, int u) {
+            const uint32_t dst = smem_base + (p & 1) * SLOT_BYTES + grp * OP_BYTES + (wq * 8 + u) * 1024;
+            const bool second = p >= psplit;
+            const uint64_t base = (second ? kbase1 : kbase0) + (uint64_t)(second ? p - psplit : p) * kstride;
+            uint32_t bytes = 0xFFFFFFF0u;
+            if (TR::a_mn) {
+                // weight gradients: k rows past the segment read as zeros
+                const int64_t rows_left = (int64_t)(k_hi - k_lo) - (int64_t)p * KP - (int64_t)hw * BK;
+                const int64_t nb = rows_left <= 0 ? 0 : rows_left * ld * 2;
+                bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
+            }
+            lds_dma16_buf(make_rsrc(base, bytes), voff[u], dst);
+        };
 
-        for (int kt = 0; kt < nk; ++kt) {
-            // ---- memory phase
-            read_stage(smem_base + (kt & (STAGES - 1)) * STAGE_BYTES);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (grp == 1) wait_next(kt, 1);
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- compute phase
-            __builtin_amdgcn_s_setprio(1);
-            const bool refill = kt + 3 < nk;
-            const int st3 = (kt + 3) & (STAGES - 1);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
-                    acc[i][j], 0, 0, 0);
-                if ((q & 3) == 1 && refill) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue_one(kt + 3, st3, q >> 2);
-                    __builtin_amdgcn_sched_barrier(0);
+        // Per-lane LDS byte offsets (within a slot, for the first k-step of a pair) of this
+        // wave's fragment reads: 4 A fragments (32 rows each) and 2 B fragments (32 columns
+        // each) per 16-k sub-step.  For the second k-step of the pair a K-major offset flips
+        // bit 6 (its chunk index is 4 higher and the swizzle only touches the low 3 bits of
+        // it), an MN-major offset moves 16 KB.
+        auto addr_k64 = [&](uint32_t op, int row, int chunk) -> uint32_t {
+            return op + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+        };
+        uint32_t a_rd[2][4], b_rd[2][2];
+    #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+    #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
+                                       : addr_k64(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
+                const int c0 = wn * 64 + j * 32;
+                b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(OP_BYTES + j * 8192, wn * 32, ks, lane)
+                            : TR::b_mn ? addr_mn(OP_BYTES, c0, ks, lane)
+                                       : addr_k64(OP_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
+            }
+        }
+
+        Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
+        auto read_step = [&](int kt) {
+            const uint32_t slot = smem_base + ((kt >> 1) & 1) * SLOT_BYTES;
+            const uint32_t hk = (uint32_t)(kt & 1) << 6;     // K-major: second k-step of the pair
+            const uint32_t hm = (uint32_t)(kt & 1) * 16384;  // MN-major: second k-step tile
+    #pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], slot + a_rd[ks][i] + hm);
+                    else ds_b128(fa[ks].q[i], slot + (a_rd[ks][i] ^ hk));
+                }
+    #pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], slot + b_rd[ks][j] + hm);
+                    else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], slot + b_rd[ks][j] + hm);
+                    else ds_b128(fb[ks].q[j], slot + (b_rd[ks][j] ^ hk));
                 }
             }
-            __builtin_amdgcn_s_setprio(0);
-            if (grp == 0) wait_next(kt, 2);
+        };
+
+
+        // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
+        // the 16 MFMAs of k-step k.  Group 0 runs M(0) C(0) M(1) C(1) ..., group 1 the same
+        // one phase later, with a block barrier between phases: while one wave of a SIMD
+        // issues MFMAs, the other reads LDS.  Pairs 0 and 1 are loaded up front; pair p+1
+        // (p >= 1) goes into the slot of pair p-1 once both groups have read it: group 1
+        // issues its eight loads between the MFMAs of C(2p-1), group 0 between those of C(2p).
+        // Pair p+1 has landed before the barrier that opens M(2p+2) of group 0: group 0 waits
+        // at the end of C(2p+1), group 1 at the end of M(2p+1).  Every wave passes 2 nk + 2
+        // barriers.
+        if (nk > 0) {
+    #pragma unroll
+            for (int u = 0; u < 8; ++u) issue_one(0, u);
+            if (np > 1) {
+    #pragma unroll
+                for (int u = 0; u < 8; ++u) issue_one(1, u);
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
+            if (grp == 1) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
+
+            for (int kt = 0; kt < nk; ++kt) {
+                const bool pair_end = (kt & 1) && (kt >> 1) + 1 < np;  // pair kt/2 + 1 due next
+                // ---- memory phase
+                read_step(kt);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (grp == 1 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- compute phase
+                __builtin_amdgcn_s_setprio(1);
+                const int pi = grp == 0 ? ((kt & 1) == 0 && kt >= 2 ? (kt >> 1) + 1 : np)
+                                        : ((kt & 1) ? ((kt + 1) >> 1) + 1 : np);
+                const bool refill = pi < np;
+    #pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
+                        acc[i][j], 0, 0, 0);
+                    if ((q & 1) && refill) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_one(pi, q >> 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                if (grp == 0 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (grp == 0) __builtin_amdgcn_s_barrier();
         }
-        if (grp == 0) __builtin_amdgcn_s_barrier();
+    } else {
+        // ---- this wave's share of the direct loads: group 0 fills the A tile of every
+        // stage, group 1 the B tile; wave wq of a group issues instructions 4wq .. 4wq+3 of
+        // the 16 that cover one 16 KB operand tile.
+        // K-major: instruction ii covers tile rows ii*16 + lane/4, physical chunk lane%4.
+        // MN-major: instruction ii covers k rows ii*2 + lane/32, physical chunk lane%32.
+        // Gate/up forward B: instruction ii covers k rows 4*(ii%8) + lane/16 of sub-tile ii/8
+        // (W_g, then W_u), physical chunk lane%16.
+        // Every operand is read through a buffer resource whose base moves with the k-step
+        // (kbase0 + kt * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed
+        // per-lane byte offset.
+        const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
+        const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
+        // row pitch (elements) of this wave's operand
+        const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
+                         : (MODE == GG_DGRAD_DOWN || MODE == GG_FWD_DOWN || MODE == GG_WGRAD_DOWN) ? d : f;
+        uint64_t kbase0, kbase1 = 0;
+        if (grp == 0) {
+            if (TR::a_mn) kbase0 = (uint64_t)(A0 + (int64_t)k_lo * ld);
+            else kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld), kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
+        } else if (MODE == GG_FWD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d);
+        } else if (MODE == GG_DGRAD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
+        } else if (MODE == GG_DGRAD_GATEUP) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
+            kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
+        } else if (MODE == GG_WGRAD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d);
+        } else if (MODE == GG_WGRAD_GATEUP) {
+            kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f);
+        } else {  // gate/up forward B: waves 0-1 of the group load W_g, waves 2-3 W_u
+            kbase0 = (uint64_t)((wq >= 2 ? B1 : B0) + (int64_t)e * d * f + n0);
+        }
+        const uint64_t kstride = mn ? (uint64_t)BK * ld * 2 : (uint64_t)BK * 2;
+        const int ksplit = MODE == GG_DGRAD_GATEUP ? f / BK : nk;
+        uint32_t voff[4];
+    #pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ii = wq * 4 + u;
+            if (MODE == GG_FWD_GATEUP && grp == 1) {
+                const int kr = 4 * (ii & 7) + (lane >> 4);
+                const int c = (lane & 15) ^ (4 * (kr & 3));
+                voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
+            } else if (!mn) {
+                const int row = ii * 16 + (lane >> 2);
+                const int c = (lane & 3) ^ swz_k(row);
+                // A: rows past the segment read any valid row (their results are not stored)
+                const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
+                voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
+            } else {
+                const int kr = ii * 2 + (lane >> 5);
+                const int c = (lane & 31) ^ swz_mn(kr);
+                const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
+                voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
+            }
+        }
+
+        // Issue the u-th of this wave's four direct loads of k-step kt into stage st.
+        auto issue_one = [&](int kt, int st, int u) {
+            const uint32_t dst = smem_base + st * STEP_STAGE_BYTES + grp * STEP_TILE_BYTES + wq * 4 * 1024 + u * 1024;
+            {
+                const bool second = kt >= ksplit;
+                const uint64_t base = (second ? kbase1 : kbase0) +
+                                      (uint64_t)(second ? kt - ksplit : kt) * kstride;
+                uint32_t bytes = 0xFFFFFFF0u;
+                if (TR::a_mn) {
+                    // weight gradients: k rows past the segment read as zeros
+                    const int64_t rows_left = (int64_t)(k_hi - k_lo) - (int64_t)kt * BK;
+                    const int64_t nb = rows_left * ld * 2;
+                    bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
+                }
+                lds_dma16_buf(make_rsrc(base, bytes), voff[u], dst);
+            }
+        };
+        auto issue = [&](int kt, int st) {
+    #pragma unroll
+            for (int u = 0; u < 4; ++u) issue_one(kt, st, u);
+        };
+
+        // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads:
+        // 4 A fragments (32 rows each) and 2 B fragments (32 columns each) per sub-step.
+        uint32_t a_rd[2][4], b_rd[2][2];
+    #pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+    #pragma unroll
+            for (int i = 0; i < 4; ++i)
+                a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
+                                       : addr_k(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
+    #pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
+                const int c0 = wn * 64 + j * 32;
+                b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(STEP_TILE_BYTES + j * 8192, wn * 32, ks, lane)
+                            : TR::b_mn ? addr_mn(STEP_TILE_BYTES, c0, ks, lane)
+                                       : addr_k(STEP_TILE_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
+            }
+        }
+
+        Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
+        auto read_stage = [&](uint32_t stage) {
+    #pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], stage + a_rd[ks][i]);
+                    else ds_b128(fa[ks].q[i], stage + a_rd[ks][i]);
+                }
+    #pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
+                    else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
+                    else ds_b128(fb[ks].q[j], stage + b_rd[ks][j]);
+                }
+            }
+        };
+
+
+        // Wait until this wave's loads of k-step kt+1 have landed, leaving the loads of
+        // the `ahead` later k-steps that exist in flight.
+        auto wait_next = [&](int kt, int ahead) {
+            if (kt + 1 >= nk) return;
+            const int newer = min(ahead, nk - 2 - kt);
+            if (newer >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (newer == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+
+        // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
+        // the 16 MFMAs of k-step k, with this wave's four loads of k-step k+3 (into the stage
+        // k-step k-1 used, which both groups have read by then) between them.  Group 0 runs
+        // M(0) C(0) M(1) C(1) ..., group 1 the same one phase later, with a block barrier
+        // between phases: while one wave of a SIMD issues MFMAs, the other reads LDS.
+        // Before the barrier that opens M(k+1) of group 0, each wave has waited for its own
+        // loads of k-step k+1: group 0 at the end of C(k) (k-steps k+2, k+3 may be in
+        // flight), group 1 at the end of M(k) (k+2 may be).  Every wave passes 2 nk + 2
+        // barriers.
+        if (nk > 0) {
+            issue(0, 0);
+            if (nk > 1) issue(1, 1);
+            if (nk > 2) issue(2, 2);
+            if (nk > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            if (grp == 1) __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+
+            for (int kt = 0; kt < nk; ++kt) {
+                // ---- memory phase
+                read_stage(smem_base + (kt & (STEP_STAGES - 1)) * STEP_STAGE_BYTES);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (grp == 1) wait_next(kt, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- compute phase
+                __builtin_amdgcn_s_setprio(1);
+                const bool refill = kt + 3 < nk;
+                const int st3 = (kt + 3) & (STEP_STAGES - 1);
+    #pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
+                        acc[i][j], 0, 0, 0);
+                    if ((q & 3) == 1 && refill) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        issue_one(kt + 3, st3, q >> 2);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                if (grp == 0) wait_next(kt, 2);
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (grp == 0) __builtin_amdgcn_s_barrier();
+        }
     }
 
     // Epilogue.  32x32 MFMA result: lane holds column (lane & 31) and rows
