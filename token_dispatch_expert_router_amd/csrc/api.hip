@@ -79,7 +79,7 @@ int64_t max_rows(const moe_desc& d) {
 size_t esize(const moe_desc& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-constexpr int kRouterBwdChunk = 256;  // tokens per partial sum of dW_router
+constexpr int kRouterBwdChunk = 64;   // tokens per partial sum of dW_router
 
 struct RouteLayout {
     size_t kcnt, list, wrt, total;

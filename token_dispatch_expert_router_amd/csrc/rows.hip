@@ -245,6 +245,7 @@ __global__ void __launch_bounds__(64) router_wgrad_partial(
     const T* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ dz, int T_,
     int d, int E, int ncol, int chunk, float* __restrict__ partial) {
     constexpr int N = Vec16<T>::N;       // i per lane
+    constexpr int U = 8;                 // tokens whose loads are in flight together
     const int lane = threadIdx.x;
     const int i0 = (blockIdx.x * 64 + lane) * N;
     const int c = blockIdx.y;
@@ -257,20 +258,29 @@ __global__ void __launch_bounds__(64) router_wgrad_partial(
     const bool ok = i0 < d;
     const int64_t tb = (int64_t)c * chunk;
     const int64_t te = min(tb + chunk, (int64_t)T_);
-    for (int64_t t = tb; t < te; ++t) {
-        float w[8];
+    for (int64_t t = tb; t < te; t += U) {
+        // issue the loads of U tokens, then their FMAs
+        u32x4 xr[U];
+        float w[U][8];
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            int e = e0 + b;
-            w[b] = (e < E) ? dl[t * E + e] : ((e == E && dz) ? dz[t] : 0.f);
+        for (int u = 0; u < U; ++u) {
+            const int64_t tt = t + u;
+            const bool in = tt < te;
+            xr[u] = (ok && in) ? *(const u32x4*)(x + tt * d + i0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int e = e0 + b;
+                w[u][b] = !in ? 0.f : (e < E) ? dl[tt * E + e] : ((e == E && dz) ? dz[tt] : 0.f);
+            }
         }
-        if (ok) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
             float xv[N];
-            Vec16<T>::unpack(*(const u32x4*)(x + t * d + i0), xv);
+            Vec16<T>::unpack(xr[u], xv);
 #pragma unroll
             for (int a = 0; a < N; ++a)
 #pragma unroll
-                for (int b = 0; b < 8; ++b) acc[a][b] += xv[a] * w[b];
+                for (int b = 0; b < 8; ++b) acc[a][b] += xv[a] * w[u][b];
         }
     }
     if (ok) {
