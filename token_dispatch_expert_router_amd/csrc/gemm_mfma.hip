@@ -240,8 +240,14 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         const int per = MT * NTl;
         e = L / per;
         const int loc = L - e * per;
-        m0 = (loc % MT) * BM;
-        n0 = (loc / MT) * BN;
+        // groups of GM m-tiles, M fastest inside a group: the 32 consecutive tiles one
+        // XCD runs at a time form a 4 x 8 block that shares 4 A and 8 B operand panels
+        constexpr int GM = 4;
+        const int gi = loc / (GM * NTl);
+        const int gm = min(GM, MT - gi * GM);
+        const int idx = loc - gi * GM * NTl;
+        m0 = (gi * GM + idx % gm) * BM;
+        n0 = (idx / gm) * BN;
         k_lo = g.offsets[e];
         k_hi = g.offsets[e + 1];
         nk = (k_hi - k_lo + BK - 1) / BK;
