@@ -164,7 +164,11 @@ __device__ __forceinline__ bf16x8_t frag_value(const Frag& f, int i) {
     return __builtin_bit_cast(bf16x8_t, f.q[i]);
 }
 
-__device__ __forceinline__ float fast_sigmoid(float a) { return 1.0f / (1.0f + __expf(-a)); }
+// Epilogue sigmoid: hardware exp and reciprocal (about 1 ulp each; the results are
+// rounded to bf16).  a -> -inf gives rcp(inf) = 0, a -> +inf gives rcp(1) = 1.
+__device__ __forceinline__ float fast_sigmoid(float a) {
+    return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+}
 
 template <int MODE> struct Traits {
     static constexpr bool a_mn = MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP;
@@ -266,6 +270,24 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Down dgrad: the SwiGLU backward of the epilogue reads a and b at every output
+    // element.  The loads of band 0 are issued before the main loop (they are older than
+    // every direct load, so the vmcnt waits of the loop still cover the loads they
+    // target), those of band i+1 before band i is processed; rows are clamped to valid
+    // rows (a row past the segment is neither used nor stored).
+    u32x4 xa[2][4], xb[2][4];
+    auto load_x = [&](int i, int buf) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int q = lane + 64 * t;
+            const int row = min(m0 + wm * 128 + i * 32 + (q >> 3), m_lim - 1);
+            const int64_t o = (int64_t)row * f + n0 + wn * 64 + (q & 7) * 8;
+            xa[buf][t] = *(const u32x4*)((const bf16_t*)g.X0 + o);
+            xb[buf][t] = *(const u32x4*)((const bf16_t*)g.X1 + o);
+        }
+    };
+    if constexpr (MODE == GG_DGRAD_DOWN) load_x(0, 0);
 
     if constexpr (TR::paired) {
         // ---- direct loads.  K-steps are loaded in pairs (64 k) into two 64 KB slots
@@ -651,6 +673,9 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     const int rq = 4 * (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        if constexpr (MODE == GG_DGRAD_DOWN) {
+            if (i + 1 < 4) load_x(i + 1, (i + 1) & 1);
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -709,8 +734,8 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                     if (row < m_lim) {
                         const int64_t o = (int64_t)row * f + n0 + ct;
                         float av[8], bv[8], dav[8], dbv[8];
-                        Vec16<bf16_t>::unpack(*(const u32x4*)((const bf16_t*)g.X0 + o), av);
-                        Vec16<bf16_t>::unpack(*(const u32x4*)((const bf16_t*)g.X1 + o), bv);
+                        Vec16<bf16_t>::unpack(xa[i & 1][t], av);
+                        Vec16<bf16_t>::unpack(xb[i & 1][t], bv);
 #pragma unroll
                         for (int u = 0; u < 8; ++u) {
                             const float sg = fast_sigmoid(av[u]);
