@@ -10,8 +10,10 @@ backward).  The workload is the Mixtral-8x22B-shaped layer: T = 4096 tokens (one
 
 Prints one JSON line.  `roofline` is for the grouped GEMM (the six launches of the
 matrix-core GEMM kernel per step, 18 * n_kept * d * f FLOPs), timed with HIP events
-on the stream the kernels run on; `hbm_kernels` gives the same for the row-movement
-calls; `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+on the stream the kernels run on, with the HBM traffic of those launches taken from
+the hardware-counter summary under profiles/ while the GEMM source is unchanged;
+`hbm_kernels` gives the same for the row-movement calls; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -131,6 +133,28 @@ def cpu_baseline(shape, inp, lay, cap):
             "seconds": round(total, 3)}
 
 
+def gemm_traffic(workload):
+    """HBM bytes per step of the six grouped-GEMM launches, from the two hardware-counter
+    passes summarised under profiles/ (FETCH_SIZE and WRITE_SIZE, scaled by what the
+    same counters read for a 1 GiB copy).  None when no summary covers this workload or
+    the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"gemm_mfma_{workload}_hbm_traffic.md")
+    src = os.path.join(ROOT, "token_dispatch_expert_router_amd", "csrc", "gemm_mfma.hip")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("machine-readable:"):
+            rec = json.loads(line.split(":", 1)[1])
+    if not rec:
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if sha != rec.get("kernel_source_sha256"):
+        return None
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +208,7 @@ def main():
     gemm_ms = calls["ffn_fwd"] + calls["ffn_bwd"] + calls.get("shared_fwd", 0) + calls.get(
         "shared_bwd", 0)
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    traffic = gemm_traffic(shape.name)
     s = 2  # bytes per bf16 element
     hbm_bytes = {
         "permute": (T + n_kept) * d * s + 4 * n_kept,
@@ -216,7 +241,9 @@ def main():
         "tflops": round((gemm_flops + router_flops) / (ms * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic["traffic_bytes_per_step"] if traffic else None,
+                     "traffic_unit": "HBM bytes per step (six launches), hardware counters",
+                     "algorithmic_bytes_per_step": (traffic or {}).get("algorithmic_bytes_per_step"),
                      "kernel": "gg_mfma_kernel (6 launches per step: fwd gate/up, fwd down, "
                                "dgrad down, wgrad down, wgrad gate/up, dgrad gate/up)",
                      "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4)},
