@@ -124,7 +124,7 @@ const char* moe_last_error(void);
 
 /* Capacity per (sub-sequence, expert): ceil(cf * S * K / E) computed in double;
  * a negative cf means dropless and returns -1.  cf = 0 gives 0 (drop everything).
- * ("capacity factor": knowledge-base notes page, prerequisites and setup.) */
+ * (capacity factor: knowledge-base notes page, prerequisites and setup.) */
 int32_t moe_capacity(int32_t S, int32_t K, int32_t E, double cf);
 
 /* Upper bound R on permuted rows: T*K when dropless, else
@@ -137,8 +137,8 @@ size_t moe_workspace_size(const moe_desc* desc, int32_t which);
 
 /* ---- forward --------------------------------------------------------------------- */
 
-/* Router (method paragraph: "router assigns by Top-K"; capacity drop per
- * sub-sequence, Section 3.3).  logits = x . w_router (+ bias), fp32 accumulation,
+/* Router (method paragraph: the router picks each token's K experts; capacity
+ * drop per sub-sequence, Section 3.3).  logits = x . w_router (+ bias), fp32 accumulation,
  * written to logits_out [T, E]; then softmax, top-K, gates, per-(sub-sequence,
  * expert) capacity drop and the permutation maps into *r.
  *   x [T, d] dtype; w_router [d, E] dtype; bias [E] float or NULL (added before the
@@ -158,13 +158,13 @@ moe_status moe_route_from_logits(const moe_desc* desc, const float* logits,
                                  const moe_routing* r, void* ws, size_t ws_bytes,
                                  void* stream);
 
-/* Permutation (method paragraph: "permutation makes tokens of the same expert
- * contiguous"): xp[row] = x[src_of[row] / K] for row < n_kept.
+/* Permutation (method paragraph: each expert's tokens are gathered into one
+ * contiguous block): xp[row] = x[src_of[row] / K] for row < n_kept.
  *   x [T, d]; xp_out [R, d]. */
 moe_status moe_permute(const moe_desc* desc, const void* x, const moe_routing* r,
                        void* xp_out, void* stream);
 
-/* Grouped SwiGLU expert FFN (method paragraph: "expert FFN computation") on the
+/* Grouped SwiGLU expert FFN (method paragraph: the experts' feed-forward step) on the
  * segments [offsets[e], offsets[e+1]) of xp:
  *   a = xp W_g,e ; b = xp W_u,e ; h = silu(a) * b (from the fp32 accumulators);
  *   o = h W_d,e.
@@ -177,7 +177,7 @@ moe_status moe_expert_ffn_fwd(const moe_desc* desc, const void* xp, const void* 
                               void* a_out, void* b_out, void* h_out, void* o_out, void* ws,
                               size_t ws_bytes, void* stream);
 
-/* Un-permutation (method paragraph: "un-permutation restores the order"), gate
+/* Un-permutation (method paragraph: rows go back to token order), gate
  * weighted: y_t = sum over kept slots k, ascending, of g_tk * o[row_of[t,k]], in
  * fp32; plus sigmoid(z_t) * shared_t when shared_out is not NULL.
  *   o [R, d]; shared_out [T, d] or NULL; sg_logit [T] float (with shared_out);

@@ -7,8 +7,8 @@
  * notes page, method paragraph and the Section 3.3 Token Dispatcher quote: the
  * router assigns each token to its Top-K experts, a permutation makes the tokens
  * of one expert contiguous, and assignments beyond an expert's capacity are
- * dropped per sub-sequence (the default drop strategy).  The pages give no
- * formula beyond "Top-K gating" and "capacity factor"; the readings fixed here
+ * dropped per sub-sequence (the default drop strategy).  The pages name Top-K
+ * gating and a capacity factor but give no formula for either; the readings fixed here
  * (softmax over all experts, top-K, gates renormalised over the K chosen,
  * capacity ceil(cf*S*K/E), drop key (p desc, t asc), expert-major then
  * token-ascending row order) are the plainest ones the rest supports.
