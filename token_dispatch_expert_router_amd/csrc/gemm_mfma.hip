@@ -72,8 +72,22 @@ constexpr int KP = 2 * BK;                              // k of one pair
 constexpr int OP_BYTES = BM * KP * 2;                   // one operand of one pair: 32 KB
 constexpr int SLOT_BYTES = 2 * OP_BYTES;                // A and B of one pair: 64 KB
 
-__device__ __forceinline__ int xcd_remap(int b, int G8) {
-    return (b & 7) * (G8 >> 3) + (b >> 3);
+// Blocks are dispatched round-robin over the 8 XCDs: block b runs on XCD b & 7.  Logical
+// tile L of `valid` goes to XCD L / ceil(valid / 8), so that each XCD runs a contiguous
+// range of equal length; returns -1 for a block with no tile.
+__device__ __forceinline__ int xcd_remap(int b, int valid) {
+    const int per = (valid + 7) >> 3;
+    const int j = b >> 3;
+    if (j >= per) return -1;
+    const int L = (b & 7) * per + j;
+    return L < valid ? L : -1;
+}
+
+// Row tiles over all segments (the grid is sized for the worst case, ceil(R/256) + E).
+__device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offsets, int E) {
+    int mt = 0;
+    for (int i = 0; i < E; ++i) mt += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    return mt;
 }
 
 // (expert, m-tile, n-tile) of logical tile L for passes with segmented rows.
@@ -221,9 +235,6 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     const int wq = wv & 3;     // wave within its group
     const int wm = wv & 1;     // output rows wm*128 .. +127 of the tile
     const int wn = wv >> 1;    // output columns wn*64 .. +63 (gate/up: features wn*32 .. +31)
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    if (L >= total_tiles) return;
-
     const int d = g.d, f = g.f;
     int e = 0, m0 = 0, m_lim = 0, n0 = 0, k_lo = 0, k_hi = 0, nk = 0;
     if (MODE <= GG_DGRAD_GATEUP) {
@@ -231,6 +242,9 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                           : MODE == GG_FWD_DOWN ? d / BN
                           : MODE == GG_DGRAD_DOWN ? f / BN
                           : d / BN;
+        // only the tiles the segments have are spread over the XCDs
+        const int L = xcd_remap(blockIdx.x, count_row_tiles(g.offsets, g.E) * n_tiles);
+        if (L < 0) return;
         int nt;
         if (!decode_rows(L, g.offsets, g.E, n_tiles, e, m0, m_lim, nt)) return;
         n0 = nt * (MODE == GG_FWD_GATEUP ? 128 : BN);
@@ -238,6 +252,8 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                     : MODE == GG_DGRAD_DOWN ? d : 2 * f;
         nk = K / BK;
     } else {
+        const int L = xcd_remap(blockIdx.x, total_tiles);
+        if (L < 0) return;
         const int Mo = MODE == GG_WGRAD_DOWN ? f : d;
         const int No = MODE == GG_WGRAD_DOWN ? d : 2 * f;
         const int MT = Mo / BM, NTl = No / BN;
