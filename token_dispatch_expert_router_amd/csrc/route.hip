@@ -243,10 +243,10 @@ __global__ void __launch_bounds__(256) topk_from_logits(const float* __restrict_
 // p (order-preserving for p >= 0) finds the threshold value and how many of the
 // candidates equal to it are kept; those are the first ones in token order.
 // ---------------------------------------------------------------------------------
-constexpr int SEL_THREADS = 256;
+constexpr int SEL_THREADS = 1024;  // one block per (sub-sequence, expert): few blocks, wide
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-    // sh: >= 8 ints of shared memory
+    // sh: >= SEL_THREADS / 64 ints of shared memory
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int incl = v;
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     int K, int capacity, uint8_t* __restrict__ keep, int32_t* __restrict__ row_of,
     int32_t* __restrict__ routed_counts, int32_t* __restrict__ kcnt, int32_t* __restrict__ cand,
     int32_t* __restrict__ kept_list) {
-    __shared__ int sh_scan[8];
+    __shared__ int sh_scan[SEL_THREADS / 64];
     __shared__ int hist[256];
     __shared__ int sh_digit, sh_above;
     const int s = blockIdx.y;

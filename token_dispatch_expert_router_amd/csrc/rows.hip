@@ -241,12 +241,15 @@ __global__ void __launch_bounds__(256) dlogits_kernel(const int32_t* __restrict_
 // columns are dl (e < E) and dz (e == E).  A wave owns 8 consecutive i (one 16-byte
 // x vector per lane... one per token) and 8 columns; chunks are summed in order later.
 template <typename T>
-__global__ void __launch_bounds__(64) router_wgrad_partial(
+__global__ void __launch_bounds__(256) router_wgrad_partial(
     const T* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ dz, int T_,
     int d, int E, int ncol, int chunk, float* __restrict__ partial) {
     constexpr int N = Vec16<T>::N;       // i per lane
     constexpr int U = 8;                 // tokens whose loads are in flight together
-    const int lane = threadIdx.x;
+    // waves 1..3 hand their sums to wave 0, lane-major (conflict-free)
+    __shared__ float red[3][N * 8][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int i0 = (blockIdx.x * 64 + lane) * N;
     const int c = blockIdx.y;
     const int e0 = blockIdx.z * 8;
@@ -256,8 +259,11 @@ __global__ void __launch_bounds__(64) router_wgrad_partial(
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
     const bool ok = i0 < d;
-    const int64_t tb = (int64_t)c * chunk;
-    const int64_t te = min(tb + chunk, (int64_t)T_);
+    // wave w sums the w-th quarter of the chunk's tokens
+    const int sub = (chunk + 3) / 4;
+    const int64_t cend = min((int64_t)(c + 1) * chunk, (int64_t)T_);
+    const int64_t tb = (int64_t)c * chunk + (int64_t)wave * sub;
+    const int64_t te = min(tb + sub, cend);
     for (int64_t t = tb; t < te; t += U) {
         // issue the loads of U tokens, then their FMAs
         u32x4 xr[U];
@@ -283,13 +289,24 @@ __global__ void __launch_bounds__(64) router_wgrad_partial(
                 for (int b = 0; b < 8; ++b) acc[a][b] += xv[a] * w[u][b];
         }
     }
-    if (ok) {
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < N; ++a)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) red[wave - 1][a * 8 + b][lane] = acc[a][b];
+    }
+    __syncthreads();
+    if (wave == 0 && ok) {
         const int ncol8 = (ncol + 7) / 8 * 8;
 #pragma unroll
         for (int a = 0; a < N; ++a)
 #pragma unroll
-            for (int b = 0; b < 8; ++b)
-                partial[((int64_t)c * d + i0 + a) * ncol8 + e0 + b] = acc[a][b];
+            for (int b = 0; b < 8; ++b) {
+                float v = acc[a][b];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) v += red[w][a * 8 + b][lane];  // fixed order
+                partial[((int64_t)c * d + i0 + a) * ncol8 + e0 + b] = v;
+            }
     }
 }
 
@@ -302,6 +319,7 @@ __global__ void __launch_bounds__(256) router_wgrad_final(const float* __restric
     if (idx >= (int64_t)d * ncol) return;
     int i = (int)(idx / ncol), e = (int)(idx % ncol);
     float s = 0.f;
+#pragma unroll 8
     for (int c = 0; c < n_chunks; ++c) s += partial[((int64_t)c * d + i) * ncol8 + e];
     if (e < E) Elem<T>::store(dw, (int64_t)i * E + e, s);
     else Elem<T>::store(dw_sg, i, s);
@@ -394,13 +412,13 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing
                                                            d.E, d.K, dlogits);
     if (d.dtype == MOE_BF16) {
         if (n_chunks > 0)
-            router_wgrad_partial<bf16_t><<<g1, 64, 0, s>>>((const bf16_t*)x, dlogits, dz, d.T, d.d,
+            router_wgrad_partial<bf16_t><<<g1, 256, 0, s>>>((const bf16_t*)x, dlogits, dz, d.T, d.d,
                                                             d.E, ncol, chunk, partial);
         router_wgrad_final<bf16_t><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
                                                        (bf16_t*)dw_router, (bf16_t*)dw_sg);
     } else {
         if (n_chunks > 0)
-            router_wgrad_partial<float><<<g1, 64, 0, s>>>((const float*)x, dlogits, dz, d.T, d.d,
+            router_wgrad_partial<float><<<g1, 256, 0, s>>>((const float*)x, dlogits, dz, d.T, d.d,
                                                            d.E, ncol, chunk, partial);
         router_wgrad_final<float><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
                                                       (float*)dw_router, (float*)dw_sg);
