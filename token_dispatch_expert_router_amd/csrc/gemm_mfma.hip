@@ -476,7 +476,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 for (int q = 0; q < 16; ++q) {
                     const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
+                        frag_value<TR::b_mn>(fb[ks], j), frag_value<TR::a_mn>(fa[ks], i),
                         acc[i][j], 0, 0, 0);
                     if ((q & 1) && refill) {
                         __builtin_amdgcn_sched_barrier(0);
@@ -657,7 +657,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 for (int q = 0; q < 16; ++q) {
                     const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        frag_value<TR::a_mn>(fa[ks], i), frag_value<TR::b_mn>(fb[ks], j),
+                        frag_value<TR::b_mn>(fb[ks], j), frag_value<TR::a_mn>(fa[ks], i),
                         acc[i][j], 0, 0, 0);
                     if ((q & 3) == 1 && refill) {
                         __builtin_amdgcn_sched_barrier(0);
@@ -675,13 +675,14 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         }
     }
 
-    // Epilogue.  32x32 MFMA result: lane holds column (lane & 31) and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r.  Each wave stages one
+    // Epilogue.  The MFMAs take the B fragment as their first operand, so each 32x32
+    // block accumulates C transposed: lane holds row (lane & 31) of the block and columns
+    // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r, four consecutive columns
+    // per group of four registers (one 16-byte LDS write).  Each wave stages one
     // 32-row band of its fp32 results (32 x 64) at a time in a private 8.5 KB of LDS,
     // then every lane handles 8-column chunks: 16-byte loads of epilogue inputs and
     // 16-byte stores.  Every wave has passed the last barrier after the last reads of
     // the operand stages, and no direct load is in flight.
-    typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
     constexpr int P = 68;  // band row pitch in floats
     const uint32_t wbase = smem_base + wv * (32 * P * 4);
@@ -695,9 +696,11 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rl = 8 * (r >> 2) + rq + (r & 3);
-                *(lds_f32*)(uintptr_t)(wbase + (rl * P + j * 32 + cl) * 4) = acc[i][j][r];
+            for (int gq = 0; gq < 4; ++gq) {
+                // row cl, columns j*32 + 8*gq + rq .. +3 of the band: one 16-byte write
+                const u32x4_t v = {__float_as_uint(acc[i][j][4 * gq]), __float_as_uint(acc[i][j][4 * gq + 1]),
+                                   __float_as_uint(acc[i][j][4 * gq + 2]), __float_as_uint(acc[i][j][4 * gq + 3])};
+                *(lds_u32x4*)(uintptr_t)(wbase + (cl * P + j * 32 + 8 * gq + rq) * 4) = v;
             }
         const int row_base = wm * 128 + i * 32;  // within the block tile
         if (MODE == GG_FWD_GATEUP) {
