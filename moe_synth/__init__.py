@@ -66,6 +66,13 @@ SHAPES = [
     # Llama3-8x70B-shaped layer, one GPU's 8192-token share of a 128K sequence, dropless.
     LayerShape("llama3_8x70b", T=8192, d=8192, E=8, K=2, f=28672, seed=4, dtype="bf16",
                cf=None, sub_seq=8192, w_std=0.02, wr_std=0.02),
+    # Mixtral-8x22B dimensions over 16384 tokens dropped per 4096-token sub-sequence
+    # (capacity 1024 per sub-sequence and expert) ...
+    LayerShape("mixtral_t16k_s4k", T=16384, d=6144, E=8, K=2, f=16384, seed=5, dtype="bf16",
+               cf=1.0, sub_seq=4096, w_std=0.02, wr_std=0.02),
+    # ... and the same tokens dropped over the full sequence (capacity 4096 per expert).
+    LayerShape("mixtral_t16k_full", T=16384, d=6144, E=8, K=2, f=16384, seed=5, dtype="bf16",
+               cf=1.0, sub_seq=16384, w_std=0.02, wr_std=0.02),
 ]
 
 

@@ -1,7 +1,9 @@
 """GPU parity at the full layer sizes, in the launch configuration bench.py times.
 
 For each bf16 layer shape (Mixtral-8x22B, Qwen2-57B-A14B with its shared expert,
-Mixtral-8x22B-G8T8 with the Zipf bias, Llama3-8x70B one GPU's share):
+Mixtral-8x22B-G8T8 with the Zipf bias, Llama3-8x70B one GPU's share, and Mixtral
+dimensions over 16384 tokens dropped per 4096-token sub-sequence or over the full
+sequence):
   - routing over all tokens: the oracle routes the GPU's logits and must match bit for bit;
   - logits of sampled tokens against the oracle's float64 GEMM;
   - the permuted buffer is an exact copy of x on sampled rows;
@@ -52,7 +54,7 @@ def _pick_tokens(topk, keep, E, rng):
 
 
 @pytest.mark.parametrize("name", ["mixtral_8x22b", "qwen2_57b_a14b", "mixtral_g8t8",
-                                  "llama3_8x70b"])
+                                  "llama3_8x70b", "mixtral_t16k_s4k", "mixtral_t16k_full"])
 def test_fullsize_parity(name):
     from token_dispatch_expert_router_amd.layer import MoELayer
     s = moe_synth.shape_by_name(name)
