@@ -210,18 +210,24 @@ def permute(x, src_of, K: int) -> np.ndarray:
     return _f64(x)[src // K]
 
 
-def ffn_rows_fwd(xp_rows, wg, wu, wd, storage: str):
-    """SwiGLU expert on some rows of one expert: returns a, b, h, o as stored."""
+def ffn_rows_fwd(xp_rows, wg, wu, wd, storage: str, o_storage: str | None = None):
+    """SwiGLU expert on some rows of one expert: returns a, b, h, o as stored.
+
+    `o_storage` (default `storage`) rounds o alone: on one rank of an expert-tensor-
+    parallel group (knowledge-base notes page, method paragraph: AllGather-V shares the
+    rows inside the ETP group, ReduceScatter-V sums the expert outputs) wg, wu are
+    column slices and wd the matching row slice, so o is a partial sum kept in fp32."""
     xr = _f64(xp_rows)
     a = xr @ _f64(wg)
     b = xr @ _f64(wu)
     h = silu(a) * b                      # from the unrounded accumulators
     a_s, b_s, h_s = store(a, storage), store(b, storage), store(h, storage)
-    o = store(h_s @ _f64(wd), storage)
+    o = store(h_s @ _f64(wd), o_storage or storage)
     return a_s, b_s, h_s, o
 
 
-def expert_ffn_fwd(xp, w_gate, w_up, w_down, offsets, storage: str):
+def expert_ffn_fwd(xp, w_gate, w_up, w_down, offsets, storage: str,
+                   o_storage: str | None = None):
     """Grouped SwiGLU FFN over the expert segments [offsets[e], offsets[e+1])."""
     n = int(offsets[-1])
     f = w_gate.shape[2]
@@ -231,7 +237,7 @@ def expert_ffn_fwd(xp, w_gate, w_up, w_down, offsets, storage: str):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
             a[lo:hi], b[lo:hi], h[lo:hi], o[lo:hi] = ffn_rows_fwd(
-                xp[lo:hi], w_gate[e], w_up[e], w_down[e], storage)
+                xp[lo:hi], w_gate[e], w_up[e], w_down[e], storage, o_storage)
     return a, b, h, o
 
 
@@ -277,14 +283,17 @@ def unpermute_bwd(dy, o, row_of, gate, keep, n_rows: int, storage: str, shared=N
     return res
 
 
-def ffn_rows_bwd_data(a_s, b_s, d_o_rows, wg, wu, wd, storage: str):
-    """dgrad for some rows of one expert: returns da, db, dxp as stored."""
+def ffn_rows_bwd_data(a_s, b_s, d_o_rows, wg, wu, wd, storage: str,
+                      dxp_storage: str | None = None):
+    """dgrad for some rows of one expert: returns da, db, dxp as stored (`dxp_storage`,
+    default `storage`: on an expert-tensor-parallel rank dxp is a partial sum over the
+    rank's ffn slice, kept in fp32 like o)."""
     dh = _f64(d_o_rows) @ _f64(wd).T
     a = _f64(a_s); b = _f64(b_s)
     sg = sigmoid(a)
     da = store(dh * b * sg * (1.0 + a * (1.0 - sg)), storage)
     db = store(dh * a * sg, storage)
-    dxp = store(da @ _f64(wg).T + db @ _f64(wu).T, storage)
+    dxp = store(da @ _f64(wg).T + db @ _f64(wu).T, dxp_storage or storage)
     return da, db, dxp
 
 
@@ -305,7 +314,8 @@ def ffn_cols_bwd(a_cols, b_cols, d_o_rows, wd, cols, storage: str):
     return store(dh * b * sg * (1.0 + a * (1.0 - sg)), storage), store(dh * a * sg, storage)
 
 
-def expert_ffn_bwd(xp, a, b, h, w_gate, w_up, w_down, offsets, d_o, storage: str):
+def expert_ffn_bwd(xp, a, b, h, w_gate, w_up, w_down, offsets, d_o, storage: str,
+                   dxp_storage: str | None = None):
     """B2..B5: dgrad through down, SwiGLU backward, wgrads, dgrad through gate/up."""
     n = int(offsets[-1])
     E, d, f = w_gate.shape
@@ -316,7 +326,8 @@ def expert_ffn_bwd(xp, a, b, h, w_gate, w_up, w_down, offsets, d_o, storage: str
         if hi <= lo:
             continue          # no rows: the weight gradients of this expert are zero
         da, db, dxp[lo:hi] = ffn_rows_bwd_data(a[lo:hi], b[lo:hi], d_o[lo:hi],
-                                               w_gate[e], w_up[e], w_down[e], storage)
+                                               w_gate[e], w_up[e], w_down[e], storage,
+                                               dxp_storage)
         xr = _f64(xp[lo:hi])
         dwd[e] = _f64(h[lo:hi]).T @ _f64(d_o[lo:hi])
         dwg[e] = xr.T @ da

@@ -450,3 +450,81 @@ def test_column_restricted_ffn_equals_full():
         assert np.max(np.abs(dwg - res["dw_gate"][e][:, cols])) <= 1e-2 * np.max(np.abs(dwg))
         dwd = oracle.round_bf16(h.T @ res["d_o"][lo:hi])
         assert np.max(np.abs(dwd - res["dw_down"][e][cols, :])) <= 1e-2 * np.max(np.abs(dwd))
+
+
+def test_expert_shards_reassemble_full_ffn():
+    """One GPU's share of the experts under expert parallelism (a contiguous range of
+    experts, rows from every source) and under expert-tensor parallelism (every expert,
+    an ffn slice of each): in float64 the expert-range results are the full grouped FFN's
+    rows and weight gradients, the ffn-slice results are its columns, and the slices'
+    partial o and dxp sum to the full ones (the contraction over the ffn index splits
+    into the slices)."""
+    rng = np.random.default_rng(17)
+    d, E, f, etp = 16, 4, 24, 3
+    counts = np.array([7, 0, 11, 5])
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    n = int(offs[-1])
+    xp = rng.standard_normal((n, d))
+    wg, wu = rng.standard_normal((E, d, f)), rng.standard_normal((E, d, f))
+    wd = rng.standard_normal((E, f, d))
+    d_o = rng.standard_normal((n, d))
+    a, b, h, o = oracle.expert_ffn_fwd(xp, wg, wu, wd, offs, "f64")
+    full = oracle.expert_ffn_bwd(xp, a, b, h, wg, wu, wd, offs, d_o, "f64")
+    close = lambda u, v: np.allclose(u, v, rtol=1e-12, atol=1e-12 * np.max(np.abs(v)))
+
+    # expert range [1, 3): segments 1 and 2 of the full layer
+    lo, hi = int(offs[1]), int(offs[3])
+    lo_offs = offs[1:4] - offs[1]
+    ea, eb, eh, eo = oracle.expert_ffn_fwd(xp[lo:hi], wg[1:3], wu[1:3], wd[1:3], lo_offs, "f64")
+    assert close(eo, o[lo:hi]) and close(eh, h[lo:hi])
+    eg = oracle.expert_ffn_bwd(xp[lo:hi], ea, eb, eh, wg[1:3], wu[1:3], wd[1:3], lo_offs,
+                               d_o[lo:hi], "f64")
+    assert close(eg["dxp"], full["dxp"][lo:hi])
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert close(eg[k], full[k][1:3]), k
+    assert np.all(eg["dw_gate"][0] == 0)          # expert 1 has no rows
+
+    # ffn slices: columns of a, b, h and of the gate/up weight gradients, rows of
+    # dW_down; o and dxp are partial sums
+    o_sum = np.zeros_like(o)
+    dxp_sum = np.zeros_like(full["dxp"])
+    for r in range(etp):
+        cols = slice(r * f // etp, (r + 1) * f // etp)
+        sg, su, sd = wg[:, :, cols], wu[:, :, cols], wd[:, cols, :]
+        sa, sb, sh, so = oracle.expert_ffn_fwd(xp, sg, su, sd, offs, "f64", o_storage="f64")
+        assert close(sa, a[:, cols]) and close(sb, b[:, cols]) and close(sh, h[:, cols])
+        sgr = oracle.expert_ffn_bwd(xp, sa, sb, sh, sg, su, sd, offs, d_o, "f64",
+                                    dxp_storage="f64")
+        assert close(sgr["dw_gate"], full["dw_gate"][:, :, cols])
+        assert close(sgr["dw_up"], full["dw_up"][:, :, cols])
+        assert close(sgr["dw_down"], full["dw_down"][:, cols, :])
+        assert not close(so, o)                   # one slice alone is not the output
+        o_sum += so
+        dxp_sum += sgr["dxp"]
+    assert close(o_sum, o)
+    assert close(dxp_sum, full["dxp"])
+
+
+def test_partial_outputs_keep_fp32():
+    """With bf16 storage, o_storage / dxp_storage = "f32" rounds only those outputs to
+    fp32: they differ from the bf16-stored ones by at most half a bf16 ulp of the value,
+    and equal the fp32 rounding of the float64 product of the stored h (resp. da, db)."""
+    rng = np.random.default_rng(18)
+    d, f = 16, 32
+    xp = oracle.round_bf16(rng.standard_normal((9, d)))
+    wg, wu = oracle.round_bf16(rng.standard_normal((1, d, f)) * 0.3), oracle.round_bf16(
+        rng.standard_normal((1, d, f)) * 0.3)
+    wd = oracle.round_bf16(rng.standard_normal((1, f, d)) * 0.3)
+    offs = np.array([0, 9])
+    a, b, h, o16 = oracle.expert_ffn_fwd(xp, wg, wu, wd, offs, "bf16")
+    _, _, _, o32 = oracle.expert_ffn_fwd(xp, wg, wu, wd, offs, "bf16", o_storage="f32")
+    exact = h @ wd[0]
+    assert np.array_equal(o32, exact.astype(np.float32).astype(np.float64))
+    assert np.array_equal(o16, oracle.round_bf16(exact))
+    assert np.all(np.abs(o16 - o32) <= np.abs(o32) * 2.0 ** -8 + 1e-30)
+    d_o = oracle.round_bf16(rng.standard_normal((9, d)))
+    g16 = oracle.expert_ffn_bwd(xp, a, b, h, wg, wu, wd, offs, d_o, "bf16")
+    g32 = oracle.expert_ffn_bwd(xp, a, b, h, wg, wu, wd, offs, d_o, "bf16", dxp_storage="f32")
+    assert np.array_equal(oracle.round_bf16(g32["dxp"]), g16["dxp"])
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(g16[k], g32[k]), k
