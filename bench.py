@@ -155,6 +155,79 @@ def gemm_traffic(workload):
     return rec
 
 
+def bench_shard(args):
+    """One GPU's expert-side share of the layer spread over G GPUs: the expert FFN
+    forward + backward (six grouped-GEMM launches) on the rows its experts receive, with
+    fp32 partial o and dxp under expert-tensor parallelism.  Routing and permutation of
+    the G sources' tokens run once, untimed, to produce those rows."""
+    import torch
+    import moe_synth
+    from token_dispatch_expert_router_amd import _lib as L
+    from token_dispatch_expert_router_amd.layer import Dispatch, ExpertShard, expert_rows
+
+    L.load()
+    s = moe_synth.shard_by_name(args.shard)
+    src = s.layer
+    cap = L.moe_capacity(src.T, src.K, src.E, src.cf) if src.cf is not None else -1
+    log(f"bench: shard {s.name}: routing {s.G} x {src.T} tokens on the GPU")
+    tok = moe_synth.make_source_tokens(src, s.G, device="cuda")
+    dp = Dispatch(s.G * src.T, src.d, src.E, src.K, src.T, cap, src.torch_dtype, device="cuda")
+    dp.run(tok["x"], tok["w_router"], tok["bias"])
+    xp, loc = expert_rows(dp, s.e0, s.e1)
+    rows = xp.shape[0]
+    del tok
+    w = moe_synth.make_shard_weights(s, device="cuda")
+    d_o = moe_synth.make_shard_grad(s, rows, device="cuda")
+    sh = ExpertShard(rows, src.d, s.E_local, s.f_local, src.torch_dtype, partial=s.etp > 1,
+                     device="cuda")
+    tm = Timer(torch)
+
+    def step():
+        tm("ffn_fwd", sh.forward, xp, w, loc)
+        tm("ffn_bwd", sh.backward, xp, w, loc, d_o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tm.on = True
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    calls = tm.means_ms()
+    gemm_ms = calls["ffn_fwd"] + calls["ffn_bwd"]
+    flops = 18.0 * rows * src.d * s.f_local
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    log(f"bench: {args.steps} timed steps, {ms:.3f} ms/step; per call (ms): "
+        + ", ".join(f"{k} {v:.3f}" for k, v in calls.items()))
+    rec = {
+        "metric": "expert-shard grouped-GEMM TFLOP/s fwd+bwd on 1 MI355X",
+        "value": round(flops / (ms * 1e-3) / 1e12, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": s.name, "source": src.name, "sources": s.G,
+                   "experts": [s.e0, s.e1], "etp": s.etp, "rows": rows, "d": src.d,
+                   "ffn_local": s.f_local, "rows_per_expert": host_list(loc),
+                   "partial_fp32": s.etp > 1,
+                   "parallelism": f"one GPU's share of ep{src.E // s.E_local} x etp{s.etp}"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "gg_mfma_kernel (6 launches per step)",
+                     "flops_per_step": flops, "ms_per_step": round(gemm_ms, 4)},
+        "calls_ms": {k: round(v, 4) for k, v in calls.items()},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def host_list(t):
+    c = t.cpu().tolist()
+    return [b - a for a, b in zip(c[:-1], c[1:])]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,11 +238,18 @@ def main():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
+    ap.add_argument("--shard", default=None,
+                    help="time one GPU's expert-side share of a multi-GPU layer instead "
+                         "(mixtral_ep8, mixtral_ep4_etp2, mixtral_etp8)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's MoE layer; --gpus {args.gpus} is not supported "
               "(the cross-GPU exchanges are not part of this build)", file=sys.stderr)
         sys.exit(2)
+
+    if args.shard:
+        bench_shard(args)
+        return
 
     import torch
     import moe_synth

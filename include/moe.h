@@ -83,6 +83,16 @@ typedef struct moe_desc {
 } moe_desc;
 
 #define MOE_FLAG_VALU_GEMM 1 /* force the vector-ALU grouped GEMMs */
+/* Expert-tensor-parallel shard (knowledge-base notes page, method paragraph: the
+ * ETP group shares the dispatched rows by AllGather-V and the expert outputs are
+ * summed by ReduceScatter-V).  On one ETP rank the call gets an f-slice of every
+ * expert's weights (desc f = f / ETP), so the down GEMM's o and the gate/up dgrad's
+ * dxp are partial sums over that slice: with this flag moe_expert_ffn_fwd writes
+ * o_out and moe_expert_ffn_bwd writes dxp_out as float [R, d] (one rounding after
+ * the cross-shard sum instead of one per shard).  Every other output keeps the
+ * layer dtype.  moe_unpermute, moe_unpermute_bwd and moe_permute_bwd reject the
+ * flag with MOE_ERR_INVALID_ARG: they take rows already summed over the shards. */
+#define MOE_FLAG_F32_PARTIAL 2
 
 /* Routing results, all device pointers written by moe_route / moe_route_from_logits:
  *   topk_idx      int32 [T, K]  expert of slot k, slot 0 the most probable
@@ -169,8 +179,12 @@ moe_status moe_permute(const moe_desc* desc, const void* x, const moe_routing* r
  *   a = xp W_g,e ; b = xp W_u,e ; h = silu(a) * b (from the fp32 accumulators);
  *   o = h W_d,e.
  *   xp [R, d]; w_gate, w_up [E, d, f]; w_down [E, f, d]; offsets [E+1] (device);
- *   a_out, b_out, h_out [R, f] (a and b are kept for the backward pass); o_out [R, d].
- * The shared expert is this call with E = 1, K = 1, f = its ffn size and
+ *   a_out, b_out, h_out [R, f] (a and b are kept for the backward pass); o_out [R, d]
+ *   (float with MOE_FLAG_F32_PARTIAL).
+ * R = moe_max_rows(desc); rows from offsets[E] to R are not touched.  On the side of
+ * the expert-parallel exchange the rows come from several source GPUs: pass
+ * T = rows received, K = 1, capacity = -1 (then R = T) and the local experts'
+ * offsets.  The shared expert is this call with E = 1, K = 1, f = its ffn size and
  * offsets = {0, T} on x itself. */
 moe_status moe_expert_ffn_fwd(const moe_desc* desc, const void* xp, const void* w_gate,
                               const void* w_up, const void* w_down, const int32_t* offsets,
@@ -203,7 +217,8 @@ moe_status moe_unpermute_bwd(const moe_desc* desc, const void* dy, const void* o
  *   dW_d,e = h^T d_o ; dW_g,e = xp^T da ; dW_u,e = xp^T db ;
  *   dxp = da W_g,e^T + db W_u,e^T.
  * An expert with no rows gets zero weight gradients.
- *   a, b, h: the buffers moe_expert_ffn_fwd wrote; d_o [R, d]; dxp_out [R, d];
+ *   a, b, h: the buffers moe_expert_ffn_fwd wrote; d_o [R, d]; dxp_out [R, d]
+ *   (float with MOE_FLAG_F32_PARTIAL);
  *   dw_gate_out, dw_up_out [E, d, f]; dw_down_out [E, f, d]; ws of
  *   moe_workspace_size(desc, MOE_WS_FFN_BWD) bytes (holds da, db). */
 moe_status moe_expert_ffn_bwd(const moe_desc* desc, const void* xp, const void* a,

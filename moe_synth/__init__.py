@@ -25,7 +25,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["LayerShape", "SHAPES", "shape_by_name", "make_inputs"]
+__all__ = ["LayerShape", "SHAPES", "shape_by_name", "make_inputs", "ShardShape", "SHARDS",
+           "shard_by_name", "make_source_tokens", "make_shard_weights", "make_shard_grad"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -135,3 +136,110 @@ def make_inputs(shape: LayerShape, device="cpu", T: Optional[int] = None,
         out["ws_up"] = _expert_stack(1, s.d, s.fs, s.seed, _SLOT["ws_up"], s.w_std, dt, device)
         out["ws_down"] = _expert_stack(1, s.fs, s.d, s.seed, _SLOT["ws_down"], s.w_std, dt, device)
     return out
+
+
+# --------------------------------------------------------------------------------------
+# One GPU's expert-side share of a layer spread over G GPUs
+# --------------------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class ShardShape:
+    """The experts one GPU holds when the layer `source` runs on G GPUs.
+
+    Each of the G GPUs routes its own T tokens (one sub-sequence per GPU, so the drop is
+    per source); the rows routed to experts [e0, e1) reach this GPU.  With etp > 1 the
+    GPU holds the ffn slice [etp_rank * f / etp, (etp_rank + 1) * f / etp) of each of
+    those experts and its o and dxp are partial sums over the slice.
+
+    Recipe: x of all G sources is one [G * T, d] tensor drawn like a layer's x (same
+    seed and slot, G * T rows); the router weight is the source layer's; the local
+    weights are the source layer's expert weights (same per-expert seeds), sliced; the
+    output gradient of the received rows is drawn with the dy slot and seed * 1000 + 500.
+    """
+    name: str
+    source: str
+    G: int
+    e0: int
+    e1: int
+    etp: int = 1
+    etp_rank: int = 0
+
+    @property
+    def layer(self) -> LayerShape:
+        return shape_by_name(self.source)
+
+    @property
+    def E_local(self) -> int:
+        return self.e1 - self.e0
+
+    @property
+    def f_local(self) -> int:
+        return self.layer.f // self.etp
+
+    @property
+    def cols(self) -> slice:
+        return slice(self.etp_rank * self.f_local, (self.etp_rank + 1) * self.f_local)
+
+
+SHARDS = [
+    # Mixtral-8x22B layer over 8 GPUs (8 x 4096 tokens), capacity factor 1.0:
+    # EP 8: one expert per GPU, its rows from all 8 GPUs;
+    ShardShape("mixtral_ep8", "mixtral_8x22b", G=8, e0=0, e1=1),
+    # EP 4 x ETP 2: two experts per GPU, half of their ffn;
+    ShardShape("mixtral_ep4_etp2", "mixtral_8x22b", G=8, e0=0, e1=2, etp=2),
+    # ETP 8: every expert, an eighth of its ffn.
+    ShardShape("mixtral_etp8", "mixtral_8x22b", G=8, e0=0, e1=8, etp=8),
+]
+
+
+def shard_by_name(name: str) -> ShardShape:
+    for s in SHARDS:
+        if s.name == name:
+            return s
+    raise KeyError(name)
+
+
+def make_source_tokens(shape: LayerShape, G: int, device="cpu") -> dict:
+    """x of G source GPUs ([G * T, d], drawn as one tensor) and the router's inputs."""
+    s = shape
+    dt = s.torch_dtype
+    out = {
+        "x": _randn((G * s.T, s.d), s.seed, _SLOT["x"], 1.0, dt, device),
+        "w_router": _randn((s.d, s.E), s.seed, _SLOT["w_router"], s.wr_std, dt, device),
+        "bias": None,
+    }
+    if s.zipf_bias:
+        b = torch.tensor([1.5 * math.log(1.0 / (e + 1)) for e in range(s.E)],
+                         dtype=torch.float64).to(torch.float32)
+        out["bias"] = b.to(device)
+    return out
+
+
+def make_shard_weights(shard: ShardShape, device="cpu", layer: Optional[LayerShape] = None) -> dict:
+    """The local experts' weights, ffn-sliced: w_gate, w_up [E_local, d, f_local] and
+    w_down [E_local, f_local, d], each expert drawn in full with its own seed."""
+    s = layer or shard.layer
+    dt = s.torch_dtype
+    g_std = s.w_std if s.w_std is not None else 1.0 / math.sqrt(s.d)
+    d_std = s.w_std if s.w_std is not None else 1.0 / math.sqrt(s.f)
+    fl, c = s.f // shard.etp, slice(shard.etp_rank * (s.f // shard.etp),
+                                    (shard.etp_rank + 1) * (s.f // shard.etp))
+    El = shard.e1 - shard.e0
+    out = {"w_gate": torch.empty((El, s.d, fl), dtype=dt, device=device),
+           "w_up": torch.empty((El, s.d, fl), dtype=dt, device=device),
+           "w_down": torch.empty((El, fl, s.d), dtype=dt, device=device)}
+    for i, e in enumerate(range(shard.e0, shard.e1)):
+        for key, slot, shp, std in (("w_gate", "w_gate", (s.d, s.f), g_std),
+                                    ("w_up", "w_up", (s.d, s.f), g_std),
+                                    ("w_down", "w_down", (s.f, s.d), d_std)):
+            w = _randn(shp, s.seed, _SLOT[slot] * 1000 + 100 + e, std, dt, device)
+            out[key][i] = w[:, c] if key != "w_down" else w[c, :]
+            del w
+    return out
+
+
+def make_shard_grad(shard: ShardShape, rows: int, device="cpu",
+                    layer: Optional[LayerShape] = None) -> torch.Tensor:
+    """Gradient of the received rows' expert outputs, [rows, d]."""
+    s = layer or shard.layer
+    return _randn((rows, s.d), s.seed * 1000 + 500, _SLOT["dy"], 1.0, s.torch_dtype, device)

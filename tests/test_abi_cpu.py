@@ -98,3 +98,22 @@ def test_null_pointers_and_workspace(L):
     assert lib.moe_unpermute(ctypes.byref(d), ctypes.c_void_p(4096), ctypes.byref(fake),
                              ctypes.c_void_p(4096), None, ctypes.c_void_p(4096), None) == -1
     assert "sg_logit" in L.moe_last_error()
+
+
+def test_partial_flag_accepted_by_ffn_rejected_by_row_calls(L):
+    """MOE_FLAG_F32_PARTIAL is a valid descriptor flag (the two FFN calls take it), and
+    the row-movement calls that read o or dxp refuse it before any launch."""
+    lib = L.load()
+    d = L.make_desc(256, 64, 4, 1, 128, 256, -1, L.MOE_BF16, L.MOE_FLAG_F32_PARTIAL)
+    assert lib.moe_max_rows(ctypes.byref(d)) == 256
+    assert L.moe_workspace_size(d, L.MOE_WS_FFN_BWD) > 0
+    fake = L.Routing(*[ctypes.c_void_p(4096 * (i + 1)) for i in range(10)])
+    p = ctypes.c_void_p(4096)
+    assert lib.moe_unpermute(ctypes.byref(d), p, ctypes.byref(fake), None, None, p, None) == -1
+    assert "MOE_FLAG_F32_PARTIAL" in L.moe_last_error()
+    assert lib.moe_unpermute_bwd(ctypes.byref(d), p, p, ctypes.byref(fake), None, None, p, p,
+                                 None, None, None) == -1
+    assert "MOE_FLAG_F32_PARTIAL" in L.moe_last_error()
+    assert lib.moe_permute_bwd(ctypes.byref(d), p, ctypes.byref(fake), None, None, None, None,
+                               None, p, None, 0, None) == -1
+    assert "MOE_FLAG_F32_PARTIAL" in L.moe_last_error()

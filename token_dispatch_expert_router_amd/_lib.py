@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FLAG_VALU_GEMM = 1
+MOE_FLAG_F32_PARTIAL = 2
 MOE_WS_ROUTE, MOE_WS_FFN_FWD, MOE_WS_FFN_BWD, MOE_WS_ROUTE_BWD, MOE_WS_PERMUTE_BWD = range(5)
 
 EXPORTS = [

@@ -52,8 +52,16 @@ moe_status check_desc(const moe_desc* d) {
             d->T, d->sub_seq);
     REQUIRE(d->capacity >= -1, MOE_ERR_INVALID_ARG, "capacity = %d < -1", d->capacity);
     REQUIRE((int64_t)d->T * d->K < (int64_t)1 << 30, MOE_ERR_UNSUPPORTED, "T*K too large");
-    REQUIRE((d->flags & ~MOE_FLAG_VALU_GEMM) == 0, MOE_ERR_INVALID_ARG, "unknown flags 0x%x",
-            d->flags);
+    REQUIRE((d->flags & ~(MOE_FLAG_VALU_GEMM | MOE_FLAG_F32_PARTIAL)) == 0, MOE_ERR_INVALID_ARG,
+            "unknown flags 0x%x", d->flags);
+    return MOE_OK;
+}
+
+// The row-movement calls read o and dxp in the layer's dtype; fp32 partial sums over an
+// f shard are summed across shards (and cast) before they come back to them.
+moe_status check_no_partial(const moe_desc& d, const char* fn) {
+    REQUIRE(!(d.flags & MOE_FLAG_F32_PARTIAL), MOE_ERR_INVALID_ARG,
+            "%s does not take MOE_FLAG_F32_PARTIAL (its row buffers are in the layer dtype)", fn);
     return MOE_OK;
 }
 
@@ -247,6 +255,7 @@ moe_status moe_expert_ffn_fwd(const moe_desc* desc, const void* xp, const void* 
     if (e != hipSuccess) return hip_status(e, "gate/up GEMM");
     moe::GemmArgs b = gemm_args(d, offsets);
     b.A0 = h_out; b.B0 = w_down; b.C0 = o_out;
+    b.out_f32 = (d.flags & MOE_FLAG_F32_PARTIAL) != 0;
     return hip_status(run_gemm(d, moe::GG_FWD_DOWN, b, s), "down GEMM");
 }
 
@@ -255,6 +264,7 @@ moe_status moe_unpermute(const moe_desc* desc, const void* o, const moe_routing*
                          void* stream) {
     moe_status st;
     if ((st = check_desc(desc)) != MOE_OK) return st;
+    if ((st = check_no_partial(*desc, "moe_unpermute")) != MOE_OK) return st;
     if ((st = check_routing(r, desc->T)) != MOE_OK) return st;
     if (desc->T == 0) return MOE_OK;
     REQUIRE((o || max_rows(*desc) == 0) && y_out, MOE_ERR_INVALID_ARG, "o or y_out is NULL");
@@ -270,6 +280,7 @@ moe_status moe_unpermute_bwd(const moe_desc* desc, const void* dy, const void* o
                              float* dsg_logit_out, void* stream) {
     moe_status st;
     if ((st = check_desc(desc)) != MOE_OK) return st;
+    if ((st = check_no_partial(*desc, "moe_unpermute_bwd")) != MOE_OK) return st;
     if ((st = check_routing(r, desc->T)) != MOE_OK) return st;
     if (desc->T == 0) return MOE_OK;
     REQUIRE(dy && dgate_out && ((o && d_o_out) || max_rows(*desc) == 0), MOE_ERR_INVALID_ARG,
@@ -315,6 +326,7 @@ moe_status moe_expert_ffn_bwd(const moe_desc* desc, const void* xp, const void* 
         return hip_status(e, "gate/up wgrad GEMM");
     moe::GemmArgs g4 = gemm_args(d, offsets);
     g4.A0 = da; g4.A1 = db; g4.B0 = w_gate; g4.B1 = w_up; g4.C0 = dxp_out;
+    g4.out_f32 = (d.flags & MOE_FLAG_F32_PARTIAL) != 0;
     if (rows && (e = run_gemm(d, moe::GG_DGRAD_GATEUP, g4, s)) != hipSuccess)
         return hip_status(e, "gate/up dgrad GEMM");
     return MOE_OK;
@@ -345,6 +357,7 @@ moe_status moe_permute_bwd(const moe_desc* desc, const void* dxp, const moe_rout
                            size_t ws_bytes, void* stream) {
     moe_status st;
     if ((st = check_desc(desc)) != MOE_OK) return st;
+    if ((st = check_no_partial(*desc, "moe_permute_bwd")) != MOE_OK) return st;
     if ((st = check_routing(r, desc->T)) != MOE_OK) return st;
     const moe_desc& d = *desc;
     if (d.T == 0) return MOE_OK;

@@ -146,6 +146,7 @@ struct GemmArgs {
     void* C0;
     void* C1;
     void* C2;
+    int out_f32;  // fwd down / dgrad gate/up: C0 is fp32 (partial sums over an f shard)
 };
 
 bool mfma_shape_ok(const moe_desc& d);

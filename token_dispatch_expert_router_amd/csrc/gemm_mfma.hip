@@ -746,8 +746,15 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 const int ct = wn * 64 + cc * 8;           // column within the block tile
                 if (MODE == GG_FWD_DOWN || MODE == GG_DGRAD_GATEUP) {
                     const int row = m0 + rt;
-                    if (row < m_lim)
-                        *(u32x4*)((bf16_t*)g.C0 + (int64_t)row * d + n0 + ct) = Vec16<bf16_t>::pack(v);
+                    const int64_t o = (int64_t)row * d + n0 + ct;
+                    if (row < m_lim) {
+                        if (g.out_f32) {
+                            *(u32x4_t*)((float*)g.C0 + o) = v0;
+                            *(u32x4_t*)((float*)g.C0 + o + 4) = v1;
+                        } else {
+                            *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(v);
+                        }
+                    }
                 } else if (MODE == GG_DGRAD_DOWN) {
                     const int row = m0 + rt;
                     if (row < m_lim) {

@@ -151,7 +151,8 @@ __global__ void __launch_bounds__(256) gg_valu_kernel(GemmArgs g) {
                 st<T>(g.C1, o, b);
                 st<T>(g.C2, o, v / (1.0f + __expf(-v)) * b);
             } else if (MODE == GG_FWD_DOWN || MODE == GG_DGRAD_GATEUP) {
-                st<T>(g.C0, (int64_t)m * d + n, v);
+                if (g.out_f32) ((float*)g.C0)[(int64_t)m * d + n] = v;
+                else st<T>(g.C0, (int64_t)m * d + n, v);
             } else if (MODE == GG_DGRAD_DOWN) {
                 const int64_t o = (int64_t)m * f + n;
                 const float a = ld<T>(g.X0, o), b = ld<T>(g.X1, o);

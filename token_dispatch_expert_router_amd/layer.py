@@ -138,3 +138,88 @@ class MoELayer:
     def forward_backward(self, inp: dict, stream=None, logits: Optional[torch.Tensor] = None):
         self.forward(inp, stream, logits)
         self.backward(inp, stream)
+
+
+class Dispatch:
+    """Routing and permutation alone (moe_route -> moe_permute): the rows one GPU sends
+    into the expert-parallel exchange, expert-major."""
+
+    def __init__(self, T: int, d: int, E: int, K: int, sub_seq: int, capacity: int,
+                 dtype: torch.dtype, device="cuda"):
+        code = L.MOE_F32 if dtype == torch.float32 else L.MOE_BF16
+        self.desc = L.make_desc(T, d, E, K, 8, sub_seq, capacity, code, 0)
+        self.R = L.moe_max_rows(self.desc)
+        dev, i32, f32 = torch.device(device), torch.int32, torch.float32
+        R1 = max(self.R, 1)
+
+        def z(shape, t):
+            return torch.zeros(shape, dtype=t, device=dev)
+
+        self.rt = {
+            "topk_idx": z((T, K), i32), "topk_prob": z((T, K), f32), "topk_gate": z((T, K), f32),
+            "keep": z((T, K), torch.uint8), "row_of": z((T, K), i32), "src_of": z((R1,), i32),
+            "routed_counts": z((max(T // sub_seq, 1), E), i32), "kept_counts": z((E,), i32),
+            "offsets": z((E + 1,), i32), "n_kept": z((1,), i32),
+        }
+        self.routing = L.make_routing(self.rt)
+        self.logits = z((T, E), f32)
+        self.xp = z((R1, d), dtype)
+        n = L.moe_workspace_size(self.desc, L.MOE_WS_ROUTE)
+        self.ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+
+    def run(self, x, w_router, bias=None, stream=None):
+        L.moe_route(self.desc, x, w_router, bias, None, self.logits, None, self.routing, self.ws,
+                    stream)
+        L.moe_permute(self.desc, x, self.routing, self.xp, stream)
+
+
+class ExpertShard:
+    """The expert FFN, forward and backward, on the rows one GPU's experts receive.
+
+    Under expert parallelism the GPU holds E experts (a contiguous range) and gets their
+    rows from every source GPU; under expert-tensor parallelism it holds an f-slice of
+    each expert and its o and dxp are partial sums that the ReduceScatter-V of the
+    exchange adds up ("MoE Parallel Folding", knowledge-base notes page, method
+    paragraph).  `partial` keeps those two outputs in float32 (MOE_FLAG_F32_PARTIAL).
+    """
+
+    def __init__(self, rows: int, d: int, E: int, f: int, dtype: torch.dtype,
+                 partial: bool = False, device="cuda", flags: int = 0):
+        code = L.MOE_F32 if dtype == torch.float32 else L.MOE_BF16
+        if partial:
+            flags |= L.MOE_FLAG_F32_PARTIAL
+        self.desc = L.make_desc(rows, d, E, 1, f, max(rows, 1), -1, code, flags)
+        self.rows, self.d, self.E, self.f = rows, d, E, f
+        dev = torch.device(device)
+        R1 = max(rows, 1)
+        out_t = torch.float32 if partial else dtype
+
+        def z(shape, t):
+            return torch.zeros(shape, dtype=t, device=dev)
+
+        self.buf = {"a": z((R1, f), dtype), "b": z((R1, f), dtype), "h": z((R1, f), dtype),
+                    "o": z((R1, d), out_t), "dxp": z((R1, d), out_t),
+                    "dw_gate": z((E, d, f), dtype), "dw_up": z((E, d, f), dtype),
+                    "dw_down": z((E, f, d), dtype)}
+        n = L.moe_workspace_size(self.desc, L.MOE_WS_FFN_BWD)
+        self.ws = torch.empty((max(n, 1),), dtype=torch.uint8, device=dev)
+
+    def forward(self, xp, w: dict, offsets, stream=None):
+        b = self.buf
+        L.moe_expert_ffn_fwd(self.desc, xp, w["w_gate"], w["w_up"], w["w_down"], offsets,
+                             b["a"], b["b"], b["h"], b["o"], None, stream)
+
+    def backward(self, xp, w: dict, offsets, d_o, stream=None):
+        b = self.buf
+        L.moe_expert_ffn_bwd(self.desc, xp, b["a"], b["b"], b["h"], w["w_gate"], w["w_up"],
+                             w["w_down"], offsets, d_o, b["dxp"], b["dw_gate"], b["dw_up"],
+                             b["dw_down"], self.ws, stream)
+
+
+def expert_rows(dp: Dispatch, e0: int, e1: int):
+    """The permuted rows of experts [e0, e1) (a view of dp.xp, they are contiguous) and
+    their offsets from 0.  Reads the offsets on the host: a set-up step, it synchronises."""
+    offs = dp.rt["offsets"].to("cpu", torch.int64)
+    lo, hi = int(offs[e0]), int(offs[e1])
+    loc = (offs[e0:e1 + 1] - lo).to(device=dp.xp.device, dtype=torch.int32)
+    return dp.xp[lo:hi], loc
