@@ -46,8 +46,8 @@
 // computing wave, where their issue cost hides under the MFMA pipeline.
 //
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
-// that each XCD runs a contiguous range, in which consecutive tiles share their
-// weight tile (M fastest) and stay in that XCD's L2.
+// that each XCD runs a contiguous range, in which consecutive tiles form 4 x 8 blocks
+// (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2.
 #include "common.h"
 
 namespace moe {
@@ -90,6 +90,19 @@ __device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offse
     return mt;
 }
 
+// Tiles of one segment (or one expert's weight gradient) are ordered in groups of
+// GROUP_M m-tiles, m fastest inside a group, so the ~32 consecutive tiles one XCD runs
+// at a time form a 4 x 8 block that shares 4 row panels and 8 weight panels, however
+// many m-tiles the segment has.
+constexpr int GROUP_M = 4;
+__device__ __forceinline__ void grouped_mn(int loc, int mt, int n_tiles, int& mi, int& ni) {
+    const int gi = loc / (GROUP_M * n_tiles);
+    const int gm = min(GROUP_M, mt - gi * GROUP_M);
+    const int idx = loc - gi * GROUP_M * n_tiles;
+    mi = gi * GROUP_M + idx % gm;
+    ni = idx / gm;
+}
+
 // (expert, m-tile, n-tile) of logical tile L for passes with segmented rows.
 __device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ offsets, int E,
                                             int n_tiles, int& e, int& m0, int& m_lim, int& nt) {
@@ -99,11 +112,11 @@ __device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ o
         const int mt = (hi - lo + BM - 1) / BM;
         const int tiles = mt * n_tiles;
         if (L < acc + tiles) {
-            const int loc = L - acc;
+            int mi;
+            grouped_mn(L - acc, mt, n_tiles, mi, nt);
             e = i;
-            m0 = lo + (loc % mt) * BM;
+            m0 = lo + mi * BM;
             m_lim = hi;
-            nt = loc / mt;
             return true;
         }
         acc += tiles;
@@ -259,15 +272,10 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         const int MT = Mo / BM, NTl = No / BN;
         const int per = MT * NTl;
         e = L / per;
-        const int loc = L - e * per;
-        // groups of GM m-tiles, M fastest inside a group: the 32 consecutive tiles one
-        // XCD runs at a time form a 4 x 8 block that shares 4 A and 8 B operand panels
-        constexpr int GM = 4;
-        const int gi = loc / (GM * NTl);
-        const int gm = min(GM, MT - gi * GM);
-        const int idx = loc - gi * GM * NTl;
-        m0 = (gi * GM + idx % gm) * BM;
-        n0 = (idx / gm) * BN;
+        int mi, ni;
+        grouped_mn(L - e * per, MT, NTl, mi, ni);
+        m0 = mi * BM;
+        n0 = ni * BN;
         k_lo = g.offsets[e];
         k_hi = g.offsets[e + 1];
         nk = (k_hi - k_lo + BK - 1) / BK;
