@@ -16,8 +16,12 @@
 //   WGRAD_GATEUP dW_g,e = xp_e^T da_e, dW_u,e = xp_e^T db_e
 //
 // Tiling.  256 x 256 output tile, k-step 32, 512 threads = 8 waves; wave w computes
-// rows 128*(w & 1) .. +127 and columns 64*(w >> 1) .. +63 of the tile as 4 x 2
-// v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane, two waves per SIMD).
+// rows 128*(w & 1) .. +127 and columns 64*(w >> 1) .. +63 of the tile as 8 x 4
+// v_mfma_f32_16x16x32_bf16 blocks (128 fp32 accumulators per lane, two waves per SIMD).
+// A fragment holds 16 rows (columns) x 8 consecutive k per lane group of 16, so one
+// k-step is a single 32-deep MFMA per block; with changing operand data the 16x16x32
+// form sustains a higher clock than 32x32x16 under the power limit (it reads and
+// writes half the accumulator bytes per FLOP).
 //
 // Data path.  Operand tiles go from global memory straight into LDS with direct
 // buffer loads (buffer_load_dwordx4 ... lds: no register staging, no LDS store
@@ -39,7 +43,7 @@
 //
 // Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
 // the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
-// compute phase C(k): the 16 MFMAs of k-step k with this wave's share of the direct
+// compute phase C(k): the 32 MFMAs of k-step k with this wave's share of the direct
 // loads between them -- one phase apart, separated by block barriers, so that on
 // every SIMD one wave issues MFMAs while the other reads LDS.  The LDS reads of one
 // phase take about as long as its MFMAs, and the direct loads are issued by the
@@ -55,7 +59,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
@@ -130,7 +134,10 @@ __device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ o
 // rows r, r+1 differ in bit 3 of the bank group while (r >> 1) & 7 spreads the eight
 // row pairs, so the 16 reads hit distinct banks.  MN-major tile [32 k][256 cols]
 // (512-byte rows): physical chunk p of k-row r holds logical chunk p ^ swz_mn(r).
-__device__ __forceinline__ int swz_mn(int r) { return (r & 3) << 2; }
+__device__ __forceinline__ int swz_mn(int r) { return ((r & 3) << 2) ^ (((r >> 3) & 1) << 1); }
+// Gate/up sub-tile [32 k][128 cols] (256-byte k rows): physical chunk = logical chunk ^
+// swz_split(k row).
+__device__ __forceinline__ int swz_split(int r) { return (4 * (r & 3)) ^ (((r >> 3) & 1) << 1); }
 // K-major single-k-step tile [256 rows][32 k] (64-byte rows): physical chunk p of row r
 // holds logical chunk p ^ swz_k(r).
 __device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
@@ -153,37 +160,38 @@ __device__ __forceinline__ uint32_t addr_k(uint32_t tile, int row, int chunk) {
     return tile + row * 64 + ((chunk ^ swz_k(row)) << 4);
 }
 // Byte address of the first of the two transpose reads of an MN-major fragment:
-// columns [c0, c0+32) of the tile, k rows 16*ks + [0, 16); the second read is 4 k rows
-// (2048 bytes) further, with the same swizzle.
-__device__ __forceinline__ uint32_t addr_mn(uint32_t tile, int c0, int ks, int lane) {
+// columns [c0, c0+16) of the tile; lane group g = lane/16 reads k rows 8g + [0, 4) and, in
+// the second read 4 k rows (2048 bytes) further with the same swizzle, 8g + [4, 8).
+__device__ __forceinline__ uint32_t addr_mn(uint32_t tile, int c0, int lane) {
     const int g = lane >> 4, s = lane & 15;
-    const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
-    const int kr = 16 * ks + 8 * (g >> 1) + (s >> 2);
+    const int col = c0 + 4 * (s & 3);
+    const int kr = 8 * g + (s >> 2);
     return tile + kr * 512 + (((col >> 3) ^ swz_mn(kr)) << 4) + (col & 7) * 2;
 }
 
 // Gate/up forward B tile: two sub-tiles [32 k][128 cols] (W_g columns, then W_u), 256-byte
-// k rows, physical chunk = logical chunk ^ 4*(k & 3).  A 32-lane half of a transpose
-// read covers 4 consecutive k rows x 64 bytes, which this swizzle spreads over all 64
-// banks.  The second read of a fragment is 4 k rows (1024 bytes) further.
-__device__ __forceinline__ uint32_t addr_mn_split(uint32_t sub, int c0, int ks, int lane) {
+// k rows, physical chunk = logical chunk ^ swz_split(k).  A 32-lane half of a transpose
+// read covers k rows 8g + [0, 4) for two lane groups g, 32 bytes each, which the swizzle
+// spreads over all 64 banks.  The second read of a fragment is 4 k rows (1024 bytes)
+// further.
+__device__ __forceinline__ uint32_t addr_mn_split(uint32_t sub, int c0, int lane) {
     const int g = lane >> 4, s = lane & 15;
-    const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
-    const int kr = 16 * ks + 8 * (g >> 1) + (s >> 2);
-    return sub + kr * 256 + (((col >> 3) ^ (4 * (kr & 3))) << 4) + (col & 7) * 2;
+    const int col = c0 + 4 * (s & 3);
+    const int kr = 8 * g + (s >> 2);
+    return sub + kr * 256 + (((col >> 3) ^ swz_split(kr)) << 4) + (col & 7) * 2;
 }
 __device__ __forceinline__ void ds_tr_pair_1k(s16x4_t& lo, s16x4_t& hi, uint32_t addr) {
     lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)addr);
     hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + 1024));
 }
 
-struct Frag {
-    s16x4_t lo[4], hi[4];  // MN-major fragments (two transpose reads)
-    u32x4_t q[4];          // K-major fragments (one read)
+template <int N> struct Frag {
+    s16x4_t lo[N], hi[N];  // MN-major fragments (two transpose reads)
+    u32x4_t q[N];          // K-major fragments (one read)
 };
 
-template <bool MN>
-__device__ __forceinline__ bf16x8_t frag_value(const Frag& f, int i) {
+template <bool MN, int N>
+__device__ __forceinline__ bf16x8_t frag_value(const Frag<N>& f, int i) {
     if (MN) {
         s16x8_t v = __builtin_shufflevector(f.lo[i], f.hi[i], 0, 1, 2, 3, 4, 5, 6, 7);
         return __builtin_bit_cast(bf16x8_t, v);
@@ -287,13 +295,13 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     const bf16_t* B1 = (const bf16_t*)g.B1;
     const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-    f32x16_t acc[4][2];
+    f32x4_t acc[8][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
     // Down dgrad: the SwiGLU backward of the epilogue reads a and b at every output
     // element.  The loads of band 0 are issued before the main loop (they are older than
@@ -364,7 +372,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             const int jj = ii & 15;
             if (MODE == GG_FWD_GATEUP && grp == 1) {
                 const int kr = 4 * (jj & 7) + (lane >> 4);
-                const int c = (lane & 15) ^ (4 * (kr & 3));
+                const int c = (lane & 15) ^ swz_split(kr);
                 voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
             } else if (!mn) {
                 const int row = ii * 8 + (lane >> 3);
@@ -403,47 +411,42 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         auto addr_k64 = [&](uint32_t op, int row, int chunk) -> uint32_t {
             return op + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
         };
-        uint32_t a_rd[2][4], b_rd[2][2];
+        uint32_t a_rd[8], b_rd[4];
     #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int i = 0; i < 8; ++i)
+            a_rd[i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 16, lane)
+                               : addr_k64(0, wm * 128 + i * 16 + (lane & 15), lane >> 4);
     #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
-                                       : addr_k64(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
-    #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
-                const int c0 = wn * 64 + j * 32;
-                b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(OP_BYTES + j * 8192, wn * 32, ks, lane)
-                            : TR::b_mn ? addr_mn(OP_BYTES, c0, ks, lane)
-                                       : addr_k64(OP_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
-            }
+        for (int j = 0; j < 4; ++j) {
+            // gate/up: j = 0, 1 read the W_g sub-tile, j = 2, 3 the W_u sub-tile
+            const int c0 = wn * 64 + j * 16;
+            b_rd[j] = MODE == GG_FWD_GATEUP ? addr_mn_split(OP_BYTES + (j >> 1) * 8192, wn * 32 + (j & 1) * 16, lane)
+                    : TR::b_mn ? addr_mn(OP_BYTES, c0, lane)
+                               : addr_k64(OP_BYTES, c0 + (lane & 15), lane >> 4);
         }
 
-        Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
+        Frag<8> fa;
+        Frag<4> fb;
         auto read_step = [&](int kt) {
             const uint32_t slot = smem_base + ((kt >> 1) & 1) * SLOT_BYTES;
             const uint32_t hk = (uint32_t)(kt & 1) << 6;     // K-major: second k-step of the pair
             const uint32_t hm = (uint32_t)(kt & 1) * 16384;  // MN-major: second k-step tile
     #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int i = 0; i < 8; ++i) {
+                if (TR::a_mn) ds_tr_pair(fa.lo[i], fa.hi[i], slot + a_rd[i] + hm);
+                else ds_b128(fa.q[i], slot + (a_rd[i] ^ hk));
+            }
     #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], slot + a_rd[ks][i] + hm);
-                    else ds_b128(fa[ks].q[i], slot + (a_rd[ks][i] ^ hk));
-                }
-    #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], slot + b_rd[ks][j] + hm);
-                    else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], slot + b_rd[ks][j] + hm);
-                    else ds_b128(fb[ks].q[j], slot + (b_rd[ks][j] ^ hk));
-                }
+            for (int j = 0; j < 4; ++j) {
+                if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb.lo[j], fb.hi[j], slot + b_rd[j] + hm);
+                else if (TR::b_mn) ds_tr_pair(fb.lo[j], fb.hi[j], slot + b_rd[j] + hm);
+                else ds_b128(fb.q[j], slot + (b_rd[j] ^ hk));
             }
         };
 
 
         // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
-        // the 16 MFMAs of k-step k.  Group 0 runs M(0) C(0) M(1) C(1) ..., group 1 the same
+        // the 32 MFMAs of k-step k.  Group 0 runs M(0) C(0) M(1) C(1) ..., group 1 the same
         // one phase later, with a block barrier between phases: while one wave of a SIMD
         // issues MFMAs, the other reads LDS.  Pairs 0 and 1 are loaded up front; pair p+1
         // (p >= 1) goes into the slot of pair p-1 once both groups have read it: group 1
@@ -481,14 +484,13 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                                         : ((kt & 1) ? ((kt + 1) >> 1) + 1 : np);
                 const bool refill = pi < np;
     #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        frag_value<TR::b_mn>(fb[ks], j), frag_value<TR::a_mn>(fa[ks], i),
-                        acc[i][j], 0, 0, 0);
-                    if ((q & 1) && refill) {
+                for (int q = 0; q < 32; ++q) {
+                    const int i = q >> 2, j = q & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        frag_value<TR::b_mn>(fb, j), frag_value<TR::a_mn>(fa, i), acc[i][j], 0, 0, 0);
+                    if ((q & 3) == 1 && refill) {
                         __builtin_amdgcn_sched_barrier(0);
-                        issue_one(pi, q >> 1);
+                        issue_one(pi, q >> 2);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -542,7 +544,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             const int ii = wq * 4 + u;
             if (MODE == GG_FWD_GATEUP && grp == 1) {
                 const int kr = 4 * (ii & 7) + (lane >> 4);
-                const int c = (lane & 15) ^ (4 * (kr & 3));
+                const int c = (lane & 15) ^ swz_split(kr);
                 voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
             } else if (!mn) {
                 const int row = ii * 16 + (lane >> 2);
@@ -581,39 +583,34 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         };
 
         // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads:
-        // 4 A fragments (32 rows each) and 2 B fragments (32 columns each) per sub-step.
-        uint32_t a_rd[2][4], b_rd[2][2];
+        // 8 A fragments (16 rows each) and 4 B fragments (16 columns each).
+        uint32_t a_rd[8], b_rd[4];
     #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int i = 0; i < 8; ++i)
+            a_rd[i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 16, lane)
+                               : addr_k(0, wm * 128 + i * 16 + (lane & 15), lane >> 4);
     #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a_rd[ks][i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 32, ks, lane)
-                                       : addr_k(0, wm * 128 + i * 32 + (lane & 31), 2 * ks + (lane >> 5));
-    #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                // gate/up: j = 0 reads the W_g sub-tile, j = 1 the W_u sub-tile
-                const int c0 = wn * 64 + j * 32;
-                b_rd[ks][j] = MODE == GG_FWD_GATEUP ? addr_mn_split(STEP_TILE_BYTES + j * 8192, wn * 32, ks, lane)
-                            : TR::b_mn ? addr_mn(STEP_TILE_BYTES, c0, ks, lane)
-                                       : addr_k(STEP_TILE_BYTES, c0 + (lane & 31), 2 * ks + (lane >> 5));
-            }
+        for (int j = 0; j < 4; ++j) {
+            // gate/up: j = 0, 1 read the W_g sub-tile, j = 2, 3 the W_u sub-tile
+            const int c0 = wn * 64 + j * 16;
+            b_rd[j] = MODE == GG_FWD_GATEUP ? addr_mn_split(STEP_TILE_BYTES + (j >> 1) * 8192, wn * 32 + (j & 1) * 16, lane)
+                    : TR::b_mn ? addr_mn(STEP_TILE_BYTES, c0, lane)
+                               : addr_k(STEP_TILE_BYTES, c0 + (lane & 15), lane >> 4);
         }
 
-        Frag fa[2], fb[2];  // [sub-step]; fb uses entries 0..1
+        Frag<8> fa;
+        Frag<4> fb;
         auto read_stage = [&](uint32_t stage) {
     #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
+            for (int i = 0; i < 8; ++i) {
+                if (TR::a_mn) ds_tr_pair(fa.lo[i], fa.hi[i], stage + a_rd[i]);
+                else ds_b128(fa.q[i], stage + a_rd[i]);
+            }
     #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (TR::a_mn) ds_tr_pair(fa[ks].lo[i], fa[ks].hi[i], stage + a_rd[ks][i]);
-                    else ds_b128(fa[ks].q[i], stage + a_rd[ks][i]);
-                }
-    #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
-                    else if (TR::b_mn) ds_tr_pair(fb[ks].lo[j], fb[ks].hi[j], stage + b_rd[ks][j]);
-                    else ds_b128(fb[ks].q[j], stage + b_rd[ks][j]);
-                }
+            for (int j = 0; j < 4; ++j) {
+                if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb.lo[j], fb.hi[j], stage + b_rd[j]);
+                else if (TR::b_mn) ds_tr_pair(fb.lo[j], fb.hi[j], stage + b_rd[j]);
+                else ds_b128(fb.q[j], stage + b_rd[j]);
             }
         };
 
@@ -629,7 +626,7 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         };
 
         // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
-        // the 16 MFMAs of k-step k, with this wave's four loads of k-step k+3 (into the stage
+        // the 32 MFMAs of k-step k, with this wave's four loads of k-step k+3 (into the stage
         // k-step k-1 used, which both groups have read by then) between them.  Group 0 runs
         // M(0) C(0) M(1) C(1) ..., group 1 the same one phase later, with a block barrier
         // between phases: while one wave of a SIMD issues MFMAs, the other reads LDS.
@@ -662,14 +659,13 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 const bool refill = kt + 3 < nk;
                 const int st3 = (kt + 3) & (STEP_STAGES - 1);
     #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int ks = q >> 3, i = (q >> 1) & 3, j = q & 1;
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        frag_value<TR::b_mn>(fb[ks], j), frag_value<TR::a_mn>(fa[ks], i),
-                        acc[i][j], 0, 0, 0);
-                    if ((q & 3) == 1 && refill) {
+                for (int q = 0; q < 32; ++q) {
+                    const int i = q >> 2, j = q & 3;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        frag_value<TR::b_mn>(fb, j), frag_value<TR::a_mn>(fa, i), acc[i][j], 0, 0, 0);
+                    if ((q & 7) == 2 && refill) {
                         __builtin_amdgcn_sched_barrier(0);
-                        issue_one(kt + 3, st3, q >> 2);
+                        issue_one(kt + 3, st3, q >> 3);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -683,10 +679,10 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
         }
     }
 
-    // Epilogue.  The MFMAs take the B fragment as their first operand, so each 32x32
-    // block accumulates C transposed: lane holds row (lane & 31) of the block and columns
-    // 8*(r/4) + 4*(lane/32) + (r%4) for accumulator register r, four consecutive columns
-    // per group of four registers (one 16-byte LDS write).  Each wave stages one
+    // Epilogue.  The MFMAs take the B fragment as their first operand, so each 16x16
+    // block accumulates C transposed: lane holds row (lane & 15) of the block and the
+    // four consecutive columns 4*(lane/16) + r, r = 0..3 (one 16-byte LDS write).  Each
+    // wave stages one
     // 32-row band of its fp32 results (32 x 64) at a time in a private 8.5 KB of LDS,
     // then every lane handles 8-column chunks: 16-byte loads of epilogue inputs and
     // 16-byte stores.  Every wave has passed the last barrier after the last reads of
@@ -694,21 +690,22 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
     constexpr int P = 68;  // band row pitch in floats
     const uint32_t wbase = smem_base + wv * (32 * P * 4);
-    const int cl = lane & 31;
-    const int rq = 4 * (lane >> 5);
+    const int cl = lane & 15;
+    const int cq = 4 * (lane >> 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (MODE == GG_DGRAD_DOWN) {
             if (i + 1 < 4) load_x(i + 1, (i + 1) & 1);
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                // row cl, columns j*32 + 8*gq + rq .. +3 of the band: one 16-byte write
-                const u32x4_t v = {__float_as_uint(acc[i][j][4 * gq]), __float_as_uint(acc[i][j][4 * gq + 1]),
-                                   __float_as_uint(acc[i][j][4 * gq + 2]), __float_as_uint(acc[i][j][4 * gq + 3])};
-                *(lds_u32x4*)(uintptr_t)(wbase + (cl * P + j * 32 + 8 * gq + rq) * 4) = v;
+            for (int j = 0; j < 4; ++j) {
+                // block row 2i + h: band row 16h + cl, columns 16j + cq .. +3: one 16-byte write
+                const f32x4_t& a4 = acc[2 * i + h][j];
+                const u32x4_t v = {__float_as_uint(a4[0]), __float_as_uint(a4[1]),
+                                   __float_as_uint(a4[2]), __float_as_uint(a4[3])};
+                *(lds_u32x4*)(uintptr_t)(wbase + ((16 * h + cl) * P + 16 * j + cq) * 4) = v;
             }
         const int row_base = wm * 128 + i * 32;  // within the block tile
         if (MODE == GG_FWD_GATEUP) {
