@@ -5,34 +5,92 @@
 // un-permutation restores token order, and the backward pass runs the duals.  These
 // kernels are pure HBM streams: every row is moved with 16-byte vector accesses,
 // one wavefront per row, with several loads in flight per lane.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
 namespace {
 
 constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 4 waves per block
-constexpr int UNROLL = 4;
 
-// xp[r] = x[src_of[r] / K] for r < n_kept.
-__global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ x,
-                                                      const int32_t* __restrict__ src_of,
-                                                      const int32_t* __restrict__ n_kept, int K,
-                                                      int vpr, u32x4* __restrict__ xp) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
-    if (r >= n_kept[0]) return;
-    const int64_t t = src_of[r] / K;
-    const u32x4* src = x + t * vpr;
-    u32x4* dst = xp + r * vpr;
-    int c = lane;
-    for (; c + 64 * (UNROLL - 1) < vpr; c += 64 * UNROLL) {
-        u32x4 v[UNROLL];
+// Chunks of a row handled by one lane per batch: lane handles chunks c0 + lane + 64u,
+// u < CHUNKS, and issues the loads of a whole batch before using any of them, so that
+// every lane keeps CHUNKS 16-byte loads in flight per source row (rows of d = 6144 bf16
+// are two batches).
+constexpr int CHUNKS = 6;
+
+// A batch that lies wholly inside the row (FULL) is loaded and stored without per-chunk
+// predicates, so that all its loads issue back to back; the row's last partial batch
+// checks every chunk.
+template <bool FULL, int U>
+__device__ __forceinline__ void load_batch(const u32x4* __restrict__ row, int c0, int lane, int vpr,
+                                           u32x4 (&v)[U]) {
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = src[c + 64 * u];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) dst[c + 64 * u] = v[u];
+    for (int u = 0; u < U; ++u) {
+        const int c = c0 + lane + 64 * u;
+        if (FULL || c < vpr) v[u] = row[c];
     }
-    for (; c < vpr; c += 64) dst[c] = src[c];
+}
+
+// Runs body(c0, std::integral_constant<bool, FULL>) for every batch of U chunks per lane.
+template <int U = CHUNKS, typename F>
+__device__ __forceinline__ void for_batches(int vpr, F&& body) {
+    int c0 = 0;
+    for (; c0 + 64 * U <= vpr; c0 += 64 * U) body(c0, std::true_type{});
+    if (c0 < vpr) body(c0, std::false_type{});
+}
+
+// The token a wave works on, as a wave-uniform value: its per-slot routing entries are
+// then read with scalar loads inside the loops instead of being kept in arrays.
+__device__ __forceinline__ int64_t wave_token() {
+    return __builtin_amdgcn_readfirstlane((int)(blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6)));
+}
+
+// acc[u] += w * row[c0 + lane + 64u] for one batch.
+template <typename T, bool FULL>
+__device__ __forceinline__ void add_batch(const u32x4* __restrict__ row, float w, int c0, int lane,
+                                          int vpr, float (&acc)[CHUNKS][Vec16<T>::N]) {
+    constexpr int N = Vec16<T>::N;
+    u32x4 v[CHUNKS];
+    load_batch<FULL>(row, c0, lane, vpr, v);
+#pragma unroll
+    for (int u = 0; u < CHUNKS; ++u) {
+        float f[N];
+        Vec16<T>::unpack(v[u], f);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[u][i] += w * f[i];
+    }
+}
+
+// xp[row_of[t,k]] = x[t] for every kept slot (t, k): token-major, so that each row of x
+// is read once and stored to its kept rows (the same xp as gathering xp[r] =
+// x[src_of[r] / K] row by row, with half the reads at K = 2).
+__global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ x,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const uint8_t* __restrict__ keep, int ntok,
+                                                      int K, int vpr, u32x4* __restrict__ xp) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = wave_token();
+    if (t >= ntok) return;
+    int nk = 0;
+    for (int k = 0; k < K; ++k) nk += keep[t * K + k] ? 1 : 0;
+    if (nk == 0) return;
+    const u32x4* src = x + t * vpr;
+    for_batches(vpr, [&](int c0, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        u32x4 v[CHUNKS];
+        load_batch<FULL>(src, c0, lane, vpr, v);
+        for (int k = 0; k < K; ++k) {
+            if (!keep[t * K + k]) continue;
+            u32x4* dst = xp + (int64_t)row_of[t * K + k] * vpr;
+#pragma unroll
+            for (int u = 0; u < CHUNKS; ++u) {
+                const int c = c0 + lane + 64 * u;
+                if (FULL || c < vpr) dst[c] = v[u];
+            }
+        }
+    });
 }
 
 // y_t = sum_{kept k, ascending} g_tk o[row_of[t,k]]  (+ sigmoid(z_t) shared_t)
@@ -44,41 +102,34 @@ __global__ void __launch_bounds__(256) unpermute_kernel(
     u32x4* __restrict__ y) {
     constexpr int N = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    const int64_t t = wave_token();
     if (t >= ntok) return;
-    int64_t rows[8];
-    float g[8];
-    int nk = 0;
-    for (int k = 0; k < K; ++k) {
-        if (keep[t * K + k]) {
-            rows[nk] = row_of[t * K + k];
-            g[nk] = gate[t * K + k];
-            ++nk;
-        }
-    }
     const float s = shared ? sigmoid_f(z[t]) : 0.f;
-    for (int c = lane; c < vpr; c += 64) {
-        float acc[N];
+    for_batches(vpr, [&](int c0, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        float acc[CHUNKS][N];
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] = 0.f;
-        for (int j = 0; j < nk; ++j) {
-            float v[N];
-            Vec16<T>::unpack(o[rows[j] * vpr + c], v);
+        for (int u = 0; u < CHUNKS; ++u)
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += g[j] * v[i];
+            for (int i = 0; i < N; ++i) acc[u][i] = 0.f;
+        for (int k = 0; k < K; ++k) {
+            if (!keep[t * K + k]) continue;
+            add_batch<T, FULL>(o + (int64_t)row_of[t * K + k] * vpr, gate[t * K + k], c0, lane, vpr,
+                               acc);
         }
-        if (shared) {
-            float v[N];
-            Vec16<T>::unpack(shared[t * vpr + c], v);
+        if (shared) add_batch<T, FULL>(shared + t * vpr, s, c0, lane, vpr, acc);
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += s * v[i];
+        for (int u = 0; u < CHUNKS; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (FULL || c < vpr) y[t * vpr + c] = Vec16<T>::pack(acc[u]);
         }
-        y[t * vpr + c] = Vec16<T>::pack(acc);
-    }
+    });
 }
 
 // d_o[row_of[t,k]] = g_tk dy_t ; dgate_tk = <dy_t, o[row_of[t,k]]> ;
 // shared: dshared_t = s_t dy_t, dz_t = <dy_t, shared_t> s_t (1 - s_t).
+// Each batch of dy is loaded once and used for every kept slot; the slot loop is unrolled
+// to its maximum (8) so that the per-slot dot products stay in registers.
 template <typename T>
 __global__ void __launch_bounds__(256) unpermute_bwd_kernel(
     const u32x4* __restrict__ dy, const u32x4* __restrict__ o, const int32_t* __restrict__ row_of,
@@ -88,58 +139,56 @@ __global__ void __launch_bounds__(256) unpermute_bwd_kernel(
     float* __restrict__ dz) {
     constexpr int N = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    const int64_t t = wave_token();
     if (t >= ntok) return;
-    int64_t rows[8];
-    float g[8];
-    float dot[8];
-    int kk[8];
-    int nk = 0;
-    for (int k = 0; k < K; ++k) {
-        if (keep[t * K + k]) {
-            rows[nk] = row_of[t * K + k];
-            g[nk] = gate[t * K + k];
-            kk[nk] = k;
-            dot[nk] = 0.f;
-            ++nk;
-        } else if (lane == 0) {
-            dgate[t * K + k] = 0.f;
-        }
-    }
     const float s = shared ? sigmoid_f(z[t]) : 0.f;
-    float sdot = 0.f;
-    for (int c = lane; c < vpr; c += 64) {
-        float dv[N];
-        Vec16<T>::unpack(dy[t * vpr + c], dv);
-        for (int j = 0; j < nk; ++j) {
-            float ov[N], w[N];
-            Vec16<T>::unpack(o[rows[j] * vpr + c], ov);
-            float acc = 0.f;
+    float dot[8], sdot = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dot[k] = 0.f;
+    // one batch: dot += <dy, r>, out = w * dy
+    auto pair = [&](auto full, const u32x4 (&dvr)[CHUNKS], const u32x4* __restrict__ r, float w,
+                    u32x4* __restrict__ out, int c0) -> float {
+        constexpr bool FULL = decltype(full)::value;
+        u32x4 rv[CHUNKS];
+        load_batch<FULL>(r, c0, lane, vpr, rv);
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < CHUNKS; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (!FULL && c >= vpr) continue;
+            float dv[N], rf[N], wv[N];
+            Vec16<T>::unpack(dvr[u], dv);
+            Vec16<T>::unpack(rv[u], rf);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
-                acc += dv[i] * ov[i];
-                w[i] = g[j] * dv[i];
+                acc += dv[i] * rf[i];
+                wv[i] = w * dv[i];
             }
-            dot[j] += acc;
-            d_o[rows[j] * vpr + c] = Vec16<T>::pack(w);
+            out[c] = Vec16<T>::pack(wv);
         }
-        if (shared) {
-            float sv[N], w[N];
-            Vec16<T>::unpack(shared[t * vpr + c], sv);
+        return acc;
+    };
+    for_batches(vpr, [&](int c0, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        u32x4 dvr[CHUNKS];
+        load_batch<FULL>(dy + t * vpr, c0, lane, vpr, dvr);
 #pragma unroll
-            for (int i = 0; i < N; ++i) {
-                sdot += dv[i] * sv[i];
-                w[i] = s * dv[i];
-            }
-            dshared[t * vpr + c] = Vec16<T>::pack(w);
+        for (int k = 0; k < 8; ++k) {
+            if (k >= K) break;
+            if (!keep[t * K + k]) continue;
+            const int64_t row = row_of[t * K + k];
+            dot[k] += pair(full, dvr, o + row * vpr, gate[t * K + k], d_o + row * vpr, c0);
         }
-    }
-    for (int j = 0; j < nk; ++j) {
-        float v = wave_sum(dot[j]);
-        if (lane == 0) dgate[t * K + kk[j]] = v;
+        if (shared) sdot += pair(full, dvr, shared + t * vpr, s, dshared + t * vpr, c0);
+    });
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k >= K) break;
+        const float v = keep[t * K + k] ? wave_sum(dot[k]) : 0.f;
+        if (lane == 0) dgate[t * K + k] = v;
     }
     if (shared) {
-        float v = wave_sum(sdot);
+        const float v = wave_sum(sdot);
         if (lane == 0) dz[t] = v * s * (1.f - s);
     }
 }
@@ -164,6 +213,7 @@ __global__ void __launch_bounds__(256) transpose_rw_kernel(const T* __restrict__
 }
 
 // dx_t = sum_{kept k} dxp[row_of[t,k]] + sum_k dl[t,e_k] w_rt[e_k] + dz_t w_sg + dx_add_t
+// (terms added in this order)
 template <typename T>
 __global__ void __launch_bounds__(256) permute_bwd_kernel(
     const u32x4* __restrict__ dxp, const int32_t* __restrict__ row_of,
@@ -173,52 +223,33 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
     int vpr, u32x4* __restrict__ dx) {
     constexpr int N = Vec16<T>::N;
     const int lane = threadIdx.x & 63;
-    const int64_t t = (int64_t)blockIdx.x * ROWS_PER_BLOCK + (threadIdx.x >> 6);
+    const int64_t t = wave_token();
     if (t >= ntok) return;
-    int64_t rows[8];
-    int nk = 0;
-    for (int k = 0; k < K; ++k)
-        if (keep[t * K + k]) rows[nk++] = row_of[t * K + k];
-    int rexp[9];
-    float rw[9];
-    int nr = 0;
-    if (dlogits) {
+    for_batches(vpr, [&](int c0, auto full) {
+        constexpr bool FULL = decltype(full)::value;
+        float acc[CHUNKS][N];
+#pragma unroll
+        for (int u = 0; u < CHUNKS; ++u)
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[u][i] = 0.f;
         for (int k = 0; k < K; ++k) {
-            int e = topk_idx[t * K + k];
-            rexp[nr] = e;
-            rw[nr] = dlogits[t * E + e];
-            ++nr;
+            if (!keep[t * K + k]) continue;
+            add_batch<T, FULL>(dxp + (int64_t)row_of[t * K + k] * vpr, 1.0f, c0, lane, vpr, acc);
         }
-    }
-    if (dz) {
-        rexp[nr] = E;
-        rw[nr] = dz[t];
-        ++nr;
-    }
-    for (int c = lane; c < vpr; c += 64) {
-        float acc[N];
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] = 0.f;
-        for (int j = 0; j < nk; ++j) {
-            float v[N];
-            Vec16<T>::unpack(dxp[rows[j] * vpr + c], v);
-#pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += v[i];
+        if (dlogits) {
+            for (int k = 0; k < K; ++k) {
+                const int e = topk_idx[t * K + k];
+                add_batch<T, FULL>(w_rt + (int64_t)e * vpr, dlogits[t * E + e], c0, lane, vpr, acc);
+            }
         }
-        for (int j = 0; j < nr; ++j) {
-            float v[N];
-            Vec16<T>::unpack(w_rt[(int64_t)rexp[j] * vpr + c], v);
+        if (dz) add_batch<T, FULL>(w_rt + (int64_t)E * vpr, dz[t], c0, lane, vpr, acc);
+        if (dx_add) add_batch<T, FULL>(dx_add + t * vpr, 1.0f, c0, lane, vpr, acc);
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += rw[j] * v[i];
+        for (int u = 0; u < CHUNKS; ++u) {
+            const int c = c0 + lane + 64 * u;
+            if (FULL || c < vpr) dx[t * vpr + c] = Vec16<T>::pack(acc[u]);
         }
-        if (dx_add) {
-            float v[N];
-            Vec16<T>::unpack(dx_add[t * vpr + c], v);
-#pragma unroll
-            for (int i = 0; i < N; ++i) acc[i] += v[i];
-        }
-        dx[t * vpr + c] = Vec16<T>::pack(acc);
-    }
+    });
 }
 
 // dl for the K chosen experts: g_j (dgate_j - sum_k g_k dgate_k); 0 elsewhere.
@@ -333,9 +364,9 @@ hipError_t launch_permute(const moe_desc& d, int64_t R, const void* x, const moe
                           void* xp, hipStream_t s) {
     const int esz = d.dtype == MOE_BF16 ? 2 : 4;
     const int vpr = d.d * esz / 16;
-    if (R > 0)
-        permute_kernel<<<blocks_for(R, ROWS_PER_BLOCK), 256, 0, s>>>(
-            (const u32x4*)x, r.src_of, r.n_kept, d.K, vpr, (u32x4*)xp);
+    if (R > 0 && d.T > 0)
+        permute_kernel<<<blocks_for(d.T, ROWS_PER_BLOCK), 256, 0, s>>>(
+            (const u32x4*)x, r.row_of, r.keep, d.T, d.K, vpr, (u32x4*)xp);
     return hipGetLastError();
 }
 
