@@ -103,16 +103,18 @@ __device__ void softmax_topk_token(float logit, int E, int K, int64_t t,
 }
 
 // ---------------------------------------------------------------------------------
-// Router GEMM, bf16 on MFMA: a block of 4 waves takes 16 tokens; the waves split d
-// (split-K) and each computes 16 tokens x 16*NB expert columns with
-// v_mfma_f32_16x16x32_bf16; the four partial sums are added in a fixed order in LDS.
-// Column E (if present) is the shared expert's gate vector w_sg.
+// Router GEMM, bf16 on MFMA: a block of W waves takes 16 tokens; the waves split d
+// (split-K, W = 8 when d % 256 == 0, else 4) and each computes 16 tokens x 16*NB expert
+// columns with v_mfma_f32_16x16x32_bf16, keeping RT_LOADS 16-byte loads of x per lane in
+// flight (the kernel streams x once and is bound by HBM); the W partial sums are added
+// in a fixed order in LDS. Column E (if present) is the shared expert's gate vector w_sg.
 // ---------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int RT_TOK = 16;     // tokens per block
 constexpr int RT_NBMAX = 5;    // up to 80 columns (64 experts + shared gate)
+constexpr int RT_LOADS = 8;    // k-steps of x loaded ahead per lane
 
 // w_rt: [NB*16][d] bf16, the router weight transposed (row e = column e of w_router,
 // row E = w_sg, zero rows after).
@@ -130,18 +132,19 @@ __global__ void __launch_bounds__(256) transpose_router_w(const bf16_t* __restri
     w_rt[i] = v;
 }
 
-__global__ void __launch_bounds__(256) router_fwd_mfma(
+template <int W>
+__global__ void __launch_bounds__(64 * W) router_fwd_mfma(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_rt, const float* __restrict__ bias,
     float* __restrict__ logits, float* __restrict__ sg_logit, int T, int d, int E, int K,
     int NB, int has_sg, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
     float* __restrict__ topk_gate) {
-    __shared__ float part[4][RT_TOK][RT_NBMAX * 16 + 1];
+    __shared__ float part[W][RT_TOK][RT_NBMAX * 16 + 1];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int t0 = blockIdx.x * RT_TOK;
     const int row = lane & 15;      // token within the block (A) / column (B)
     const int kq = lane >> 4;       // which 8-wide k group of the 32
-    const int dslice = d / 4;
+    const int dslice = d / W;
     const int kbeg = wave * dslice;
 
     f32x4_t acc[RT_NBMAX];
@@ -150,19 +153,29 @@ __global__ void __launch_bounds__(256) router_fwd_mfma(
 
     const int tok = t0 + row;
     const bool tok_ok = tok < T;
+    // rows past T read token 0 (a valid row) and are zeroed
     const bf16_t* xa = x + (int64_t)(tok_ok ? tok : 0) * d + kbeg + kq * 8;
-    for (int k = 0; k < dslice; k += 32) {
-        u32x4 av = tok_ok ? *(const u32x4*)(xa + k) : u32x4{0, 0, 0, 0};
-        bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+    const bf16_t* wb0 = w_rt + (int64_t)row * d + kbeg + kq * 8;
+    auto step = [&](const u32x4& av, int k) {
+        const u32x4 az = tok_ok ? av : u32x4{0, 0, 0, 0};
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, az);
 #pragma unroll
         for (int j = 0; j < RT_NBMAX; ++j) {
             if (j < NB) {
-                const bf16_t* wb = w_rt + (int64_t)(j * 16 + row) * d + kbeg + kq * 8 + k;
-                bf16x8_t b = __builtin_bit_cast(bf16x8_t, *(const u32x4*)wb);
+                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb0 + (int64_t)j * 16 * d + k));
                 acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
             }
         }
+    };
+    int k = 0;
+    for (; k + 32 * RT_LOADS <= dslice; k += 32 * RT_LOADS) {
+        u32x4 av[RT_LOADS];
+#pragma unroll
+        for (int u = 0; u < RT_LOADS; ++u) av[u] = *(const u32x4*)(xa + k + 32 * u);
+#pragma unroll
+        for (int u = 0; u < RT_LOADS; ++u) step(av[u], k + 32 * u);
     }
+    for (; k < dslice; k += 32) step(*(const u32x4*)(xa + k), k);
     // D layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4)+i.
 #pragma unroll
     for (int j = 0; j < RT_NBMAX; ++j) {
@@ -172,21 +185,26 @@ __global__ void __launch_bounds__(256) router_fwd_mfma(
         }
     }
     __syncthreads();
-    // Each wave finishes 4 tokens: fixed-order sum of the 4 split-K partials, bias,
-    // then softmax and top-K with one lane per expert.
-    for (int q = 0; q < RT_TOK / 4; ++q) {
-        int tl = wave * (RT_TOK / 4) + q;
+    // Each wave finishes RT_TOK / W tokens: fixed-order sum of the W split-K partials,
+    // bias, then softmax and top-K with one lane per expert.
+    auto colsum = [&](int tl, int c) {
+        float v = part[0][tl][c];
+#pragma unroll
+        for (int w = 1; w < W; ++w) v += part[w][tl][c];
+        return v;
+    };
+    for (int q = 0; q < RT_TOK / W; ++q) {
+        int tl = wave * (RT_TOK / W) + q;
         int t = t0 + tl;
         if (t >= T) break;
         float l = 0.f;
         if (lane < E) {
-            l = ((part[0][tl][lane] + part[1][tl][lane]) + part[2][tl][lane]) + part[3][tl][lane];
+            l = colsum(tl, lane);
             if (bias) l = l + bias[lane];
             logits[(int64_t)t * E + lane] = l;
         }
         // the shared gate is column E, which can be past the last lane (E = 64)
-        if (has_sg && lane == 0)
-            sg_logit[t] = ((part[0][tl][E] + part[1][tl][E]) + part[2][tl][E]) + part[3][tl][E];
+        if (has_sg && lane == 0) sg_logit[t] = colsum(tl, E);
         softmax_topk_token(l, E, K, t, topk_idx, topk_prob, topk_gate);
     }
 }
@@ -389,6 +407,132 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     if (tid == 0) kcnt[g] = ktot;
 }
 
+// The same selection with each thread's candidates held in registers (a sub-sequence
+// of at most SEL_THREADS * SEL_PER tokens): thread i owns tokens i*per .. i*per+per-1 and
+// has at most one candidate slot per token, so candidate j of the thread sits at the
+// fixed register index j and every pass reads registers instead of global memory.
+constexpr int SEL_PER = 16;
+
+template <int PER>
+__global__ void __launch_bounds__(SEL_THREADS) select_kernel_reg(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_prob, int S, int E,
+    int K, int capacity, uint8_t* __restrict__ keep, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ routed_counts, int32_t* __restrict__ kcnt,
+    int32_t* __restrict__ kept_list) {
+    __shared__ int sh_scan[SEL_THREADS / 64];
+    __shared__ int hist[256];
+    __shared__ int sh_digit, sh_above;
+    const int s = blockIdx.y;
+    const int e = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int per = (S + SEL_THREADS - 1) / SEL_THREADS;
+    const int64_t tbeg = (int64_t)s * S + (int64_t)tid * per;
+    const int64_t tend = min(tbeg + per, (int64_t)(s + 1) * S);
+    const int64_t g = (int64_t)s * E + e;
+    int32_t* my_kept = kept_list + g * S;
+
+    int slot[PER];
+    uint32_t key[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        slot[j] = -1;
+        const int64_t t = tbeg + j;
+        if (j < per && t < tend)
+            for (int k = 0; k < K; ++k)
+                if (topk_idx[t * K + k] == e) slot[j] = (int)(t * K + k);
+    }
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        key[j] = slot[j] >= 0 ? __float_as_uint(topk_prob[slot[j]]) : 0u;
+        c += slot[j] >= 0 ? 1 : 0;
+    }
+    int n;
+    block_exclusive_scan(c, sh_scan, &n);
+    if (tid == 0) routed_counts[g] = n;
+
+    uint32_t thr = 0u;
+    int want_eq = 0;
+    const bool all_kept = capacity < 0 || n <= capacity;
+    const bool none_kept = !all_kept && capacity == 0;
+    if (!all_kept && !none_kept) {
+        uint32_t prefix = 0u, pmask = 0u;
+        int want = capacity;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (slot[j] >= 0 && (key[j] & pmask) == prefix)
+                    atomicAdd(&hist[(key[j] >> shift) & 255u], 1);
+            __syncthreads();
+            if (tid < 64) {
+                // lane l owns digits 255-4l .. 252-4l (descending)
+                int hv[4];
+                int loc = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) { hv[q] = hist[255 - 4 * tid - q]; loc += hv[q]; }
+                int incl = loc;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    int nb = __shfl_up(incl, o, MOE_WAVE);
+                    if (tid >= o) incl += nb;
+                }
+                int excl = incl - loc;
+                if (excl < want && incl >= want) {
+                    int run = excl;
+                    for (int q = 0; q < 4; ++q) {
+                        if (run + hv[q] >= want) {
+                            sh_digit = 255 - 4 * tid - q;
+                            sh_above = run;
+                            break;
+                        }
+                        run += hv[q];
+                    }
+                }
+            }
+            __syncthreads();
+            want -= sh_above;
+            prefix |= ((uint32_t)sh_digit) << shift;
+            pmask |= 255u << shift;
+            __syncthreads();
+        }
+        thr = prefix;
+        want_eq = want;
+    }
+
+    // keep flags in token order; candidates equal to the threshold ranked by token
+    int eq_local = 0;
+    if (!all_kept && !none_kept) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) eq_local += (slot[j] >= 0 && key[j] == thr) ? 1 : 0;
+    }
+    int eq_tot;
+    int eq_seen = block_exclusive_scan(eq_local, sh_scan, &eq_tot);
+    uint32_t kept_mask = 0u;
+    int kc = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (slot[j] < 0) continue;
+        bool kp;
+        if (all_kept) kp = true;
+        else if (none_kept) kp = false;
+        else if (key[j] > thr) kp = true;
+        else if (key[j] == thr) kp = (eq_seen++ < want_eq);
+        else kp = false;
+        keep[slot[j]] = kp ? 1 : 0;
+        if (!kp) row_of[slot[j]] = -1;
+        kept_mask |= kp ? (1u << j) : 0u;
+        kc += kp ? 1 : 0;
+    }
+    int ktot;
+    int w = block_exclusive_scan(kc, sh_scan, &ktot);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (kept_mask & (1u << j)) my_kept[w++] = slot[j];
+    if (tid == 0) kcnt[g] = ktot;
+}
+
 // Rows of every kept assignment: experts in ascending order, then tokens ascending
 // (sub-sequences in order, token order inside each).  One block per (s, e).
 __global__ void __launch_bounds__(256) maps_kernel(const int32_t* __restrict__ kcnt,
@@ -455,9 +599,15 @@ hipError_t launch_router_fwd(const moe_desc& d, const void* x, const void* w_rou
         int64_t n = (int64_t)NB * 16 * d.d;
         transpose_router_w<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
             (const bf16_t*)w_router, (const bf16_t*)w_sg, wrt, d.d, d.E, NB * 16);
-        router_fwd_mfma<<<(d.T + RT_TOK - 1) / RT_TOK, 256, 0, s>>>(
-            (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB, w_sg ? 1 : 0,
-            r.topk_idx, r.topk_prob, r.topk_gate);
+        const unsigned nb = (d.T + RT_TOK - 1) / RT_TOK;
+        if (d.d % 256 == 0)
+            router_fwd_mfma<8><<<nb, 512, 0, s>>>(
+                (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB,
+                w_sg ? 1 : 0, r.topk_idx, r.topk_prob, r.topk_gate);
+        else
+            router_fwd_mfma<4><<<nb, 256, 0, s>>>(
+                (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB,
+                w_sg ? 1 : 0, r.topk_idx, r.topk_prob, r.topk_gate);
     } else if (d.dtype == MOE_BF16) {
         router_fwd_valu<bf16_t><<<d.T, 64, 0, s>>>(
             (const bf16_t*)x, (const bf16_t*)w_router, bias, (const bf16_t*)w_sg, logits, sg_logit,
@@ -483,9 +633,14 @@ hipError_t launch_select_and_maps(const moe_desc& d, const moe_routing& r, Route
     dim3 grid(d.E, n_sub);
     int32_t* cand = ws.list;
     int32_t* kept = ws.list + (int64_t)n_sub * d.E * d.sub_seq;
-    select_kernel<<<grid, SEL_THREADS, 0, s>>>(r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K,
-                                               d.capacity, r.keep, r.row_of, r.routed_counts,
-                                               ws.kcnt, cand, kept);
+    if (d.sub_seq <= SEL_THREADS * SEL_PER)
+        select_kernel_reg<SEL_PER><<<grid, SEL_THREADS, 0, s>>>(
+            r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K, d.capacity, r.keep, r.row_of,
+            r.routed_counts, ws.kcnt, kept);
+    else
+        select_kernel<<<grid, SEL_THREADS, 0, s>>>(r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K,
+                                                   d.capacity, r.keep, r.row_of, r.routed_counts,
+                                                   ws.kcnt, cand, kept);
     maps_kernel<<<grid, 256, 0, s>>>(ws.kcnt, kept, n_sub, d.sub_seq, d.E, r.row_of, r.src_of,
                                      r.kept_counts, r.offsets, r.n_kept);
     return hipGetLastError();

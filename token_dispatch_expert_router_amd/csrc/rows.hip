@@ -291,10 +291,11 @@ __global__ void __launch_bounds__(256) router_wgrad_partial(
         for (int b = 0; b < 8; ++b) acc[a][b] = 0.f;
     const bool ok = i0 < d;
     // wave w sums the w-th quarter of the chunk's tokens
+    // (wave-uniform bounds: the per-token dl and dz values are then scalar loads)
     const int sub = (chunk + 3) / 4;
     const int64_t cend = min((int64_t)(c + 1) * chunk, (int64_t)T_);
-    const int64_t tb = (int64_t)c * chunk + (int64_t)wave * sub;
-    const int64_t te = min(tb + sub, cend);
+    const int64_t tb = __builtin_amdgcn_readfirstlane((int)((int64_t)c * chunk + (int64_t)wave * sub));
+    const int64_t te = __builtin_amdgcn_readfirstlane((int)min(tb + sub, cend));
     for (int64_t t = tb; t < te; t += U) {
         // issue the loads of U tokens, then their FMAs
         u32x4 xr[U];
