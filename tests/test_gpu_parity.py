@@ -68,6 +68,11 @@ CASES = {
     # the same on the vector-ALU router (d not a multiple of 128)
     "shared_e64_valu": _shape("shared_e64_valu", T=128, d=200, E=64, K=4, f=136, fs=72, sub_seq=128,
                               seed=20, w_std=0.05),
+    # fp32 with 16 experts (the router weight gradient's many-column kernel, in fp32)
+    "fp32_e16": _shape("fp32_e16", T=192, d=72, E=16, K=4, f=40, sub_seq=64, cf=1.0, seed=21,
+                       dtype="f32", w_std=None, wr_std=0.5),
+    # 32 experts, dropless
+    "e32": _shape("e32", T=256, d=256, E=32, K=4, f=256, seed=22, w_std=0.05),
     # one expert, top-1: a dense SwiGLU MLP
     "dense": _shape("dense", T=300, d=256, E=1, K=1, f=512, sub_seq=300, seed=15),
 }
@@ -166,6 +171,9 @@ ROUTE_CASES = [  # T, E, K, S, cf, integer-valued logits (many exact ties)
     (2048, 64, 8, 512, 1.0, True), (1000, 16, 4, 250, 0.5, True), (512, 8, 1, 64, 1.0, False),
     (333, 5, 5, 111, 1.0, True), (8192, 8, 2, 1024, 1.25, False), (64, 64, 8, 64, 0.0, False),
     (640, 3, 2, 640, None, True), (4096, 64, 8, 4096, None, False),
+    # sub-sequences at and past the 16384 tokens the register-resident select handles
+    (16384, 8, 2, 16384, 1.0, False), (20480, 8, 2, 20480, 1.0, False),
+    (32768, 16, 4, 32768, 0.75, True),
 ]
 
 

@@ -342,6 +342,88 @@ __global__ void __launch_bounds__(256) router_wgrad_partial(
     }
 }
 
+// The same partial sums for many columns (E = 16, 32 or 64, + the shared gate) on the
+// fp32 matrix cores: per chunk the partial is the product x_c^T dcol_c (K = the chunk's
+// tokens), so a block stages the chunk's x rows for 256 consecutive i (16-byte loads) and
+// its dl/dz columns (zero-padded to a multiple of 16) in LDS, and wave w accumulates
+// i = i0 + 64w .. +63 against every column with v_mfma_f32_16x16x4_f32, four tokens per
+// instruction, tokens in order.  x is read once whatever the number of columns, and the
+// products and sums stay in fp32.
+constexpr int RW_I = 256;      // i per block
+constexpr int RW_TOK = 64;     // tokens per chunk (at most)
+constexpr int RW_CT = 5;       // 16-column tiles: up to 80 columns
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename T, int CT>
+__global__ void __launch_bounds__(256) router_wgrad_partial_wide(
+    const T* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ dz, int T_,
+    int d, int E, int ncol, int chunk, float* __restrict__ partial) {
+    __shared__ __attribute__((aligned(16))) T sx[RW_TOK][RW_I];
+    __shared__ float sw[RW_TOK][CT * 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i0 = blockIdx.x * RW_I;
+    const int c = blockIdx.y;
+    const int64_t tb = (int64_t)c * chunk;
+    const int nt = (int)min((int64_t)chunk, (int64_t)T_ - tb);
+    const int ni = min(RW_I, d - i0);
+    // stage x[tb .. tb+nt)[i0 .. i0+ni) in 16-byte pieces (d % 8 == 0, so ni is a whole
+    // number of pieces) and the columns; zeros past the ends
+    constexpr int P16 = Elem<T>::per16;
+    constexpr int CPT = RW_I / P16;
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    for (int q = tid; q < RW_TOK * CPT; q += 256) {
+        const int t = q / CPT, ch = q % CPT;
+        const bool ok = t < nt && ch * P16 < ni;
+        const v4u v = *(const v4u*)(x + (ok ? (tb + t) * d + i0 + ch * P16 : 0));
+        *(v4u*)&sx[t][ch * P16] = ok ? v : v4u{0u, 0u, 0u, 0u};
+    }
+    for (int q = tid; q < RW_TOK * CT * 16; q += 256) {
+        const int t = q / (CT * 16), e = q % (CT * 16);
+        float v = 0.f;
+        if (t < nt) v = e < E ? dl[(tb + t) * E + e] : (e == E && dz ? dz[tb + t] : 0.f);
+        sw[t][e] = v;
+    }
+    __syncthreads();
+    // A = x^T (16 i x 4 tokens): lane supplies x[t0 + lane/16][i]; B = dcol (4 tokens x 16
+    // columns): lane supplies dcol[t0 + lane/16][col]; D: lane holds rows 4*(lane/16) + r,
+    // column lane%16.
+    f32x4_t acc[4][CT];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < CT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int kr = lane >> 4, cc = lane & 15;
+    for (int t0 = 0; t0 < RW_TOK; t0 += 4) {
+        float av[4], bv[CT];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) av[a] = Elem<T>::load(&sx[t0 + kr][0], wave * 64 + a * 16 + cc);
+#pragma unroll
+        for (int b = 0; b < CT; ++b) bv[b] = sw[t0 + kr][b * 16 + cc];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < CT; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    const int ncol8 = (ncol + 7) / 8 * 8;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int il = wave * 64 + a * 16 + 4 * kr + r;
+            if (il >= ni) continue;
+            float* out = partial + ((int64_t)c * d + i0 + il) * ncol8;
+#pragma unroll
+            for (int b = 0; b < CT; ++b) {
+                const int e = b * 16 + cc;
+                if (e < ncol) out[e] = acc[a][b][r];
+            }
+        }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) router_wgrad_final(const float* __restrict__ partial,
                                                           int n_chunks, int d, int E, int ncol,
@@ -442,14 +524,36 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing
     if (d.T > 0)  // with no token the final pass alone writes zero gradients
         dlogits_kernel<<<blocks_for(d.T, 4), 256, 0, s>>>(r.topk_idx, r.topk_gate, dgate, d.T,
                                                            d.E, d.K, dlogits);
+    // many columns: the matrix-core kernel (chunks of at most RW_TOK tokens)
+    const int ct = (ncol + 15) / 16;
+    const bool wide = ncol > 8 && ct <= RW_CT && chunk <= RW_TOK && n_chunks > 0;
+    const dim3 gw(blocks_for(d.d, RW_I), n_chunks);
+    auto launch_wide = [&](auto tag) {
+        using T = decltype(tag);
+        const T* xt = (const T*)x;
+        if (ct <= 1)
+            router_wgrad_partial_wide<T, 1><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
+        else if (ct <= 2)
+            router_wgrad_partial_wide<T, 2><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
+        else if (ct <= 3)
+            router_wgrad_partial_wide<T, 3><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
+        else if (ct <= 4)
+            router_wgrad_partial_wide<T, 4><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
+        else
+            router_wgrad_partial_wide<T, 5><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
+    };
     if (d.dtype == MOE_BF16) {
-        if (n_chunks > 0)
+        if (wide)
+            launch_wide(bf16_t{});
+        else if (n_chunks > 0)
             router_wgrad_partial<bf16_t><<<g1, 256, 0, s>>>((const bf16_t*)x, dlogits, dz, d.T, d.d,
                                                             d.E, ncol, chunk, partial);
         router_wgrad_final<bf16_t><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
                                                        (bf16_t*)dw_router, (bf16_t*)dw_sg);
     } else {
-        if (n_chunks > 0)
+        if (wide)
+            launch_wide(float{});
+        else if (n_chunks > 0)
             router_wgrad_partial<float><<<g1, 256, 0, s>>>((const float*)x, dlogits, dz, d.T, d.d,
                                                            d.E, ncol, chunk, partial);
         router_wgrad_final<float><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
