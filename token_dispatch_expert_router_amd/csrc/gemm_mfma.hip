@@ -322,70 +322,37 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
     if constexpr (MODE == GG_DGRAD_DOWN) load_x(0, 0);
 
     if constexpr (TR::paired) {
+        static_assert(!TR::a_mn && !TR::b_mn, "the paired staging holds two K-major operands");
         // ---- direct loads.  K-steps are loaded in pairs (64 k) into two 64 KB slots
         // [A 32 KB | B 32 KB]; group 0 loads A, group 1 loads B, and wave wq of a group issues
         // instructions 8wq .. 8wq+7 of the 32 (1 KB each) that cover one operand of a pair.
-        //   K-major operand: [256 rows][64 k] with 128-byte rows, so that every instruction
-        //     reads whole 128-byte lines: instruction ii covers rows 8ii + lane/8, physical
-        //     chunk lane%8 (swizzle chunk ^ ((row >> 1) & 7)).
-        //   MN-major operand: two k-step tiles [32 k][256 cols] (k-step 2p at 0, 2p+1 at
-        //     16 KB); instruction ii covers tile ii/16, k rows 2(ii%16) + lane/32, physical
-        //     chunk lane%32.
-        //   Gate/up forward B: two k-step tiles, each [W_g sub-tile | W_u sub-tile];
-        //     instruction ii covers tile ii/16, sub-tile (ii/8)%2, k rows 4(ii%8) + lane/16,
-        //     physical chunk lane%16.
-        // Every load goes through a buffer resource whose base moves with the pair (kbase0 +
-        // p * kstride; the gate/up dgrad switches to kbase1 at k = f) and a fixed per-lane
-        // byte offset.
-        const bool mn = grp == 0 ? TR::a_mn : TR::b_mn;
-        const int hw = wq >> 1;  // MN-major operands: the k-step of the pair this wave loads
-        const int64_t lda = (MODE == GG_FWD_GATEUP || MODE == GG_DGRAD_DOWN) ? d : f;
-        // row pitch (elements) of this wave's operand
-        const int64_t ld = grp == 0 ? (TR::a_mn ? (MODE == GG_WGRAD_DOWN ? f : d) : lda)
-                         : (MODE == GG_DGRAD_DOWN || MODE == GG_FWD_DOWN || MODE == GG_WGRAD_DOWN) ? d : f;
-        const int64_t kofs = mn ? (int64_t)hw * BK * ld : 0;  // MN-major: first k row of this wave's k-step
+        // An operand sits as [256 rows][64 k] with 128-byte rows, so that every instruction
+        // reads whole 128-byte lines: instruction ii covers rows 8ii + lane/8, physical chunk
+        // lane%8 (swizzle chunk ^ ((row >> 1) & 7)).  Every load goes through a buffer
+        // resource whose base moves with the pair (kbase0 + p * kstride; the gate/up dgrad
+        // switches to kbase1 at k = f) and a fixed per-lane byte offset.
+        const int64_t ld = MODE == GG_DGRAD_DOWN ? d : f;  // row pitch of both operands
         uint64_t kbase0, kbase1 = 0;
         if (grp == 0) {
-            if (TR::a_mn) kbase0 = (uint64_t)(A0 + (int64_t)k_lo * ld + kofs);
-            else kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld), kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
-        } else if (MODE == GG_FWD_DOWN) {
-            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + kofs);
+            kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld);
+            if (MODE == GG_DGRAD_GATEUP) kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
         } else if (MODE == GG_DGRAD_DOWN) {
             kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
-        } else if (MODE == GG_DGRAD_GATEUP) {
+        } else {
             kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
             kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
-        } else if (MODE == GG_WGRAD_DOWN) {
-            kbase0 = (uint64_t)(B0 + (int64_t)k_lo * d + kofs);
-        } else if (MODE == GG_WGRAD_GATEUP) {
-            kbase0 = (uint64_t)((n0 < f ? B0 : B1) + (int64_t)k_lo * f + kofs);
-        } else {  // gate/up forward B: odd waves of the group load W_u, even waves W_g
-            kbase0 = (uint64_t)(((wq & 1) ? B1 : B0) + (int64_t)e * d * f + n0 + kofs);
         }
-        const uint64_t kstride = mn ? (uint64_t)KP * ld * 2 : (uint64_t)KP * 2;
+        const uint64_t kstride = (uint64_t)KP * 2;
         const int psplit = MODE == GG_DGRAD_GATEUP ? f / KP : 0x7FFFFFFF;
         const int np = (nk + 1) >> 1;
         uint32_t voff[8];
     #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int ii = wq * 8 + u;
-            const int jj = ii & 15;
-            if (MODE == GG_FWD_GATEUP && grp == 1) {
-                const int kr = 4 * (jj & 7) + (lane >> 4);
-                const int c = (lane & 15) ^ swz_split(kr);
-                voff[u] = (uint32_t)(((int64_t)kr * f + c * 8) * 2);
-            } else if (!mn) {
-                const int row = ii * 8 + (lane >> 3);
-                const int c = (lane & 7) ^ ((row >> 1) & 7);
-                // A: rows past the segment read any valid row (their results are not stored)
-                const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
-                voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
-            } else {
-                const int kr = 2 * jj + (lane >> 5);
-                const int c = (lane & 31) ^ swz_mn(kr);
-                const int col0 = grp == 0 ? m0 : (MODE == GG_WGRAD_GATEUP && n0 >= f ? n0 - f : n0);
-                voff[u] = (uint32_t)(((int64_t)kr * ld + col0 + c * 8) * 2);
-            }
+            const int row = (wq * 8 + u) * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            // A: rows past the segment read any valid row (their results are not stored)
+            const int r = grp == 0 ? min(m0 + row, m_lim - 1) - m0 : row;
+            voff[u] = (uint32_t)(((int64_t)r * ld + c * 8) * 2);
         }
 
         // Issue the u-th of this wave's eight direct loads of pair p.
@@ -393,55 +360,31 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
             const uint32_t dst = smem_base + (p & 1) * SLOT_BYTES + grp * OP_BYTES + (wq * 8 + u) * 1024;
             const bool second = p >= psplit;
             const uint64_t base = (second ? kbase1 : kbase0) + (uint64_t)(second ? p - psplit : p) * kstride;
-            uint32_t bytes = 0xFFFFFFF0u;
-            if (TR::a_mn) {
-                // weight gradients: k rows past the segment read as zeros
-                const int64_t rows_left = (int64_t)(k_hi - k_lo) - (int64_t)p * KP - (int64_t)hw * BK;
-                const int64_t nb = rows_left <= 0 ? 0 : rows_left * ld * 2;
-                bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
-            }
-            lds_dma16_buf(make_rsrc(base, bytes), voff[u], dst);
+            lds_dma16_buf(make_rsrc(base, 0xFFFFFFF0u), voff[u], dst);
         };
 
         // Per-lane LDS byte offsets (within a slot, for the first k-step of a pair) of this
-        // wave's fragment reads: 4 A fragments (32 rows each) and 2 B fragments (32 columns
-        // each) per 16-k sub-step.  For the second k-step of the pair a K-major offset flips
-        // bit 6 (its chunk index is 4 higher and the swizzle only touches the low 3 bits of
-        // it), an MN-major offset moves 16 KB.
+        // wave's fragment reads: 8 A fragments (16 rows each) and 4 B fragments (16 columns
+        // each).  For the second k-step of the pair an offset flips bit 6 (its chunk index is
+        // 4 higher and the swizzle only touches the low 3 bits of it).
         auto addr_k64 = [&](uint32_t op, int row, int chunk) -> uint32_t {
             return op + row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
         };
         uint32_t a_rd[8], b_rd[4];
     #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            a_rd[i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 16, lane)
-                               : addr_k64(0, wm * 128 + i * 16 + (lane & 15), lane >> 4);
+        for (int i = 0; i < 8; ++i) a_rd[i] = addr_k64(0, wm * 128 + i * 16 + (lane & 15), lane >> 4);
     #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // gate/up: j = 0, 1 read the W_g sub-tile, j = 2, 3 the W_u sub-tile
-            const int c0 = wn * 64 + j * 16;
-            b_rd[j] = MODE == GG_FWD_GATEUP ? addr_mn_split(OP_BYTES + (j >> 1) * 8192, wn * 32 + (j & 1) * 16, lane)
-                    : TR::b_mn ? addr_mn(OP_BYTES, c0, lane)
-                               : addr_k64(OP_BYTES, c0 + (lane & 15), lane >> 4);
-        }
+        for (int j = 0; j < 4; ++j) b_rd[j] = addr_k64(OP_BYTES, wn * 64 + j * 16 + (lane & 15), lane >> 4);
 
         Frag<8> fa;
         Frag<4> fb;
         auto read_step = [&](int kt) {
             const uint32_t slot = smem_base + ((kt >> 1) & 1) * SLOT_BYTES;
-            const uint32_t hk = (uint32_t)(kt & 1) << 6;     // K-major: second k-step of the pair
-            const uint32_t hm = (uint32_t)(kt & 1) * 16384;  // MN-major: second k-step tile
+            const uint32_t hk = (uint32_t)(kt & 1) << 6;  // second k-step of the pair
     #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if (TR::a_mn) ds_tr_pair(fa.lo[i], fa.hi[i], slot + a_rd[i] + hm);
-                else ds_b128(fa.q[i], slot + (a_rd[i] ^ hk));
-            }
+            for (int i = 0; i < 8; ++i) ds_b128(fa.q[i], slot + (a_rd[i] ^ hk));
     #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (MODE == GG_FWD_GATEUP) ds_tr_pair_1k(fb.lo[j], fb.hi[j], slot + b_rd[j] + hm);
-                else if (TR::b_mn) ds_tr_pair(fb.lo[j], fb.hi[j], slot + b_rd[j] + hm);
-                else ds_b128(fb.q[j], slot + (b_rd[j] ^ hk));
-            }
+            for (int j = 0; j < 4; ++j) ds_b128(fb.q[j], slot + (b_rd[j] ^ hk));
         };
 
 
