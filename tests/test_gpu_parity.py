@@ -71,6 +71,9 @@ CASES = {
     # fp32 with 16 experts (the router weight gradient's many-column kernel, in fp32)
     "fp32_e16": _shape("fp32_e16", T=192, d=72, E=16, K=4, f=40, sub_seq=64, cf=1.0, seed=21,
                        dtype="f32", w_std=None, wr_std=0.5),
+    # d % 256 == 128: the router GEMM splits d over 4 waves (the expert GEMMs take the
+    # vector-ALU path)
+    "d384": _shape("d384", T=320, d=384, E=8, K=2, f=128, sub_seq=160, cf=1.0, seed=23),
     # 32 experts, dropless
     "e32": _shape("e32", T=256, d=256, E=32, K=4, f=256, seed=22, w_std=0.05),
     # one expert, top-1: a dense SwiGLU MLP
