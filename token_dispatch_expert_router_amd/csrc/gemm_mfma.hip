@@ -428,7 +428,9 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 const bool refill = pi < np;
     #pragma unroll
                 for (int q = 0; q < 32; ++q) {
-                    const int i = q >> 2, j = q & 3;
+                    // snake order: consecutive MFMAs differ in one operand only (the
+                    // fewest operand changes, which lowers the matrix cores' power)
+                    const int i = q >> 2, j = (i & 1) ? 3 - (q & 3) : (q & 3);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         frag_value<TR::b_mn>(fb, j), frag_value<TR::a_mn>(fa, i), acc[i][j], 0, 0, 0);
                     if ((q & 3) == 1 && refill) {
@@ -603,7 +605,9 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                 const int st3 = (kt + 3) & (STEP_STAGES - 1);
     #pragma unroll
                 for (int q = 0; q < 32; ++q) {
-                    const int i = q >> 2, j = q & 3;
+                    // snake order: consecutive MFMAs differ in one operand only (the
+                    // fewest operand changes, which lowers the matrix cores' power)
+                    const int i = q >> 2, j = (i & 1) ? 3 - (q & 3) : (q & 3);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         frag_value<TR::b_mn>(fb, j), frag_value<TR::a_mn>(fa, i), acc[i][j], 0, 0, 0);
                     if ((q & 7) == 2 && refill) {
