@@ -3,8 +3,8 @@
 // "MoE Parallel Folding" (arXiv 2504.14960), knowledge-base notes page, method
 // paragraph: permutation gathers each expert's tokens into a contiguous block, the
 // un-permutation restores token order, and the backward pass runs the duals.  These
-// kernels are pure HBM streams: every row is moved with 16-byte vector accesses,
-// one wavefront per row, with several loads in flight per lane.
+// kernels are pure HBM streams: every row is moved with 16-byte vector accesses, one
+// wavefront per token, with a batch of loads in flight per lane and source row.
 #include <type_traits>
 
 #include "common.h"
