@@ -117,3 +117,18 @@ def test_partial_flag_accepted_by_ffn_rejected_by_row_calls(L):
     assert lib.moe_permute_bwd(ctypes.byref(d), p, ctypes.byref(fake), None, None, None, None,
                                None, p, None, 0, None) == -1
     assert "MOE_FLAG_F32_PARTIAL" in L.moe_last_error()
+
+
+def test_binding_raises_library_error(L):
+    """The Python binding turns a failed status into MoeError carrying the library's
+    message, before any launch (a null stream handle is never touched)."""
+    import types
+    s0 = types.SimpleNamespace(cuda_stream=0)
+    bad = L.make_desc(256, 64, 4, 9, 128, 256, -1, L.MOE_F32)
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_permute(bad, None, L.Routing(), None, stream=s0)
+    assert ei.value.status == -1 and "K = 9" in str(ei.value)
+    uneven = L.make_desc(100, 64, 4, 2, 128, 48, -1, L.MOE_F32)
+    with pytest.raises(L.MoeError) as ei:
+        L.moe_route_from_logits(uneven, None, L.Routing(), None, stream=s0)
+    assert "multiple" in str(ei.value)
