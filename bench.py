@@ -223,6 +223,43 @@ def bench_shard(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_route_sweep(args):
+    """Routing alone (moe_route_from_logits: softmax, top-K, drop, maps) on seeded logits of
+    T tokens, with the drop taken per 4096-token sub-sequence or over the whole sequence
+    (the selection over a gathered-logits tensor of several GPUs' tokens); one JSON line
+    per case."""
+    import torch
+    from token_dispatch_expert_router_amd import _lib as L
+    from token_dispatch_expert_router_amd.layer import Dispatch
+
+    L.load()
+    E, K, cf = 8, 2, 1.0
+    for T in (4096, 16384, 32768, 65536):
+        for S in sorted({4096, T}):
+            g = torch.Generator(device="cuda").manual_seed(T + S)
+            logits = torch.randn((T, E), generator=g, device="cuda") * 2.0
+            cap = L.moe_capacity(S, K, E, cf)
+            dp = Dispatch(T, 64, E, K, S, cap, torch.float32, device="cuda")
+            for _ in range(3):
+                L.moe_route_from_logits(dp.desc, logits, dp.routing, dp.ws)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(20):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                L.moe_route_from_logits(dp.desc, logits, dp.routing, dp.ws)
+                b.record()
+                b.synchronize()
+                times.append(a.elapsed_time(b))
+            times.sort()
+            ms = times[len(times) // 2]
+            print(json.dumps({"metric": "routing time (softmax, top-K, capacity drop, maps)",
+                              "value": round(ms * 1000.0, 2), "unit": "us", "T": T, "E": E,
+                              "K": K, "sub_seq": S, "capacity": cap,
+                              "n_kept": int(dp.rt["n_kept"].item()),
+                              "higher_is_better": False, "data": "synthetic"}), flush=True)
+
+
 def host_list(t):
     c = t.cpu().tolist()
     return [b - a for a, b in zip(c[:-1], c[1:])]
@@ -241,6 +278,9 @@ def main():
     ap.add_argument("--shard", default=None,
                     help="time one GPU's expert-side share of a multi-GPU layer instead "
                          "(mixtral_ep8, mixtral_ep4_etp2, mixtral_etp8)")
+    ap.add_argument("--route-sweep", action="store_true",
+                    help="time the routing alone over 4096..65536 tokens, dropped per "
+                         "4096-token sub-sequence or over the whole sequence")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's MoE layer; --gpus {args.gpus} is not supported "
@@ -249,6 +289,9 @@ def main():
 
     if args.shard:
         bench_shard(args)
+        return
+    if args.route_sweep:
+        bench_route_sweep(args)
         return
 
     import torch

@@ -174,9 +174,10 @@ ROUTE_CASES = [  # T, E, K, S, cf, integer-valued logits (many exact ties)
     (2048, 64, 8, 512, 1.0, True), (1000, 16, 4, 250, 0.5, True), (512, 8, 1, 64, 1.0, False),
     (333, 5, 5, 111, 1.0, True), (8192, 8, 2, 1024, 1.25, False), (64, 64, 8, 64, 0.0, False),
     (640, 3, 2, 640, None, True), (4096, 64, 8, 4096, None, False),
-    # sub-sequences at and past the 16384 tokens the register-resident select handles
+    # sub-sequences at and past the 16384 / 32768 tokens the register-resident selects
+    # handle (longer ones take the list-based kernel)
     (16384, 8, 2, 16384, 1.0, False), (20480, 8, 2, 20480, 1.0, False),
-    (32768, 16, 4, 32768, 0.75, True),
+    (32768, 16, 4, 32768, 0.75, True), (40960, 8, 2, 40960, 1.0, False),
 ]
 
 

@@ -408,9 +408,10 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
 }
 
 // The same selection with each thread's candidates held in registers (a sub-sequence
-// of at most SEL_THREADS * SEL_PER tokens): thread i owns tokens i*per .. i*per+per-1 and
-// has at most one candidate slot per token, so candidate j of the thread sits at the
-// fixed register index j and every pass reads registers instead of global memory.
+// of at most SEL_THREADS * PER tokens, PER = 16 or 32): thread i owns tokens
+// i*per .. i*per+per-1 and has at most one candidate slot per token, so candidate j of
+// the thread sits at the fixed register index j and every pass reads registers instead
+// of global memory.
 constexpr int SEL_PER = 16;
 
 template <int PER>
@@ -635,6 +636,10 @@ hipError_t launch_select_and_maps(const moe_desc& d, const moe_routing& r, Route
     int32_t* kept = ws.list + (int64_t)n_sub * d.E * d.sub_seq;
     if (d.sub_seq <= SEL_THREADS * SEL_PER)
         select_kernel_reg<SEL_PER><<<grid, SEL_THREADS, 0, s>>>(
+            r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K, d.capacity, r.keep, r.row_of,
+            r.routed_counts, ws.kcnt, kept);
+    else if (d.sub_seq <= SEL_THREADS * 2 * SEL_PER)
+        select_kernel_reg<2 * SEL_PER><<<grid, SEL_THREADS, 0, s>>>(
             r.topk_idx, r.topk_prob, d.sub_seq, d.E, d.K, d.capacity, r.keep, r.row_of,
             r.routed_counts, ws.kcnt, kept);
     else
