@@ -51,7 +51,9 @@
 //
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
 // that each XCD runs a contiguous range, in which consecutive tiles form 4 x 8 blocks
-// (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2.
+// (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2.  The
+// weight-gradient passes, whose tiles' K is their expert's segment length, give each
+// XCD an equal contiguous share of every expert instead.
 #include "common.h"
 
 namespace moe {
@@ -245,7 +247,7 @@ constexpr int NTHREADS = 512;
 template <int MODE>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
-gg_mfma_kernel(GemmArgs g, int total_tiles) {
+gg_mfma_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
     using TR = Traits<MODE>;
 
@@ -273,15 +275,23 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
                     : MODE == GG_DGRAD_DOWN ? d : 2 * f;
         nk = K / BK;
     } else {
-        const int L = xcd_remap(blockIdx.x, total_tiles);
-        if (L < 0) return;
+        // Weight gradients: a tile's K is its expert's segment, which differs between
+        // experts (up to 15x on skewed routings), so XCD x takes the same contiguous
+        // eighth of every expert's tile order, [x per / 8, (x + 1) per / 8): every XCD
+        // then has the same work whatever the segment lengths.  Block b runs the
+        // (b >> 3)-th tile of its XCD's sequence (expert-major).
         const int Mo = MODE == GG_WGRAD_DOWN ? f : d;
         const int No = MODE == GG_WGRAD_DOWN ? d : 2 * f;
         const int MT = Mo / BM, NTl = No / BN;
         const int per = MT * NTl;
-        e = L / per;
+        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+        const int lo = (int)((int64_t)x * per / 8);
+        const int cnt = (int)((int64_t)(x + 1) * per / 8) - lo;
+        if (cnt == 0) return;
+        e = j / cnt;
+        if (e >= g.E) return;
         int mi, ni;
-        grouped_mn(L - e * per, MT, NTl, mi, ni);
+        grouped_mn(lo + (j - e * cnt), MT, NTl, mi, ni);
         m0 = mi * BM;
         n0 = ni * BN;
         k_lo = g.offsets[e];
@@ -739,8 +749,8 @@ gg_mfma_kernel(GemmArgs g, int total_tiles) {
 }
 
 template <int MODE>
-hipError_t launch_mode(const GemmArgs& a, unsigned g8, int total, hipStream_t s) {
-    gg_mfma_kernel<MODE><<<g8, NTHREADS, 0, s>>>(a, total);
+hipError_t launch_mode(const GemmArgs& a, unsigned g8, hipStream_t s) {
+    gg_mfma_kernel<MODE><<<g8, NTHREADS, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -758,21 +768,21 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
         case GG_FWD_DOWN: tiles = mt_max * (a.d / BN); break;
         case GG_DGRAD_DOWN: tiles = mt_max * (a.f / BN); break;
         case GG_DGRAD_GATEUP: tiles = mt_max * (a.d / BN); break;
-        case GG_WGRAD_DOWN: tiles = (int64_t)a.E * (a.f / BM) * (a.d / BN); break;
-        default: tiles = (int64_t)a.E * (a.d / BM) * (2 * a.f / BN); break;
+        // weight gradients: every XCD runs ceil(per / 8) tiles of each expert (at most)
+        case GG_WGRAD_DOWN: tiles = (int64_t)a.E * (((int64_t)(a.f / BM) * (a.d / BN) + 7) / 8) * 8; break;
+        default: tiles = (int64_t)a.E * (((int64_t)(a.d / BM) * (2 * a.f / BN) + 7) / 8) * 8; break;
     }
     if (tiles <= 0) return hipSuccess;
     const int64_t g8 = (tiles + 7) / 8 * 8;
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const unsigned G = (unsigned)g8;
-    const int total = (int)tiles;
     switch (mode) {
-        case GG_FWD_GATEUP: return launch_mode<GG_FWD_GATEUP>(a, G, total, s);
-        case GG_FWD_DOWN: return launch_mode<GG_FWD_DOWN>(a, G, total, s);
-        case GG_DGRAD_DOWN: return launch_mode<GG_DGRAD_DOWN>(a, G, total, s);
-        case GG_DGRAD_GATEUP: return launch_mode<GG_DGRAD_GATEUP>(a, G, total, s);
-        case GG_WGRAD_DOWN: return launch_mode<GG_WGRAD_DOWN>(a, G, total, s);
-        default: return launch_mode<GG_WGRAD_GATEUP>(a, G, total, s);
+        case GG_FWD_GATEUP: return launch_mode<GG_FWD_GATEUP>(a, G, s);
+        case GG_FWD_DOWN: return launch_mode<GG_FWD_DOWN>(a, G, s);
+        case GG_DGRAD_DOWN: return launch_mode<GG_DGRAD_DOWN>(a, G, s);
+        case GG_DGRAD_GATEUP: return launch_mode<GG_DGRAD_GATEUP>(a, G, s);
+        case GG_WGRAD_DOWN: return launch_mode<GG_WGRAD_DOWN>(a, G, s);
+        default: return launch_mode<GG_WGRAD_GATEUP>(a, G, s);
     }
 }
 
