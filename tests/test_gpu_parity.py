@@ -78,6 +78,11 @@ CASES = {
     "e32": _shape("e32", T=256, d=256, E=32, K=4, f=256, seed=22, w_std=0.05),
     # one expert, top-1: a dense SwiGLU MLP
     "dense": _shape("dense", T=300, d=256, E=1, K=1, f=512, sub_seq=300, seed=15),
+    # segments of about 320 rows: every expert's last row tile holds 40-90 valid rows
+    "short_tail": _shape("short_tail", T=1280, d=512, E=8, K=2, f=1024, seed=24, w_std=0.05),
+    # segments of 50-80 rows: one mostly empty row tile per expert
+    "short_segments": _shape("short_segments", T=512, d=512, E=16, K=2, f=512, seed=25,
+                             w_std=0.05),
 }
 
 
