@@ -187,6 +187,13 @@ __device__ __forceinline__ void ds_tr_pair_1k(s16x4_t& lo, s16x4_t& hi, uint32_t
     hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(addr + 1024));
 }
 
+// Weight-gradient output: written once and not read by this layer again, so it is
+// stored nontemporally (it does not displace the operand panels in L2).
+__device__ __forceinline__ void store_stream(bf16_t* p, const u32x4& v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (u32x4_t*)p);
+}
+
 template <int N> struct Frag {
     s16x4_t lo[N], hi[N];  // MN-major fragments (two transpose reads)
     u32x4_t q[N];          // K-major fragments (one read)
@@ -735,13 +742,13 @@ gg_mfma_kernel(GemmArgs g) {
                     }
                 } else if (MODE == GG_WGRAD_DOWN) {
                     const int64_t o = (int64_t)e * f * d + (int64_t)(m0 + rt) * d + n0 + ct;
-                    *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(v);
+                    store_stream((bf16_t*)g.C0 + o, Vec16<bf16_t>::pack(v));
                 } else {  // GG_WGRAD_GATEUP
                     const bool first = n0 < f;
                     bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
                     const int64_t o = (int64_t)e * d * f + (int64_t)(m0 + rt) * f +
                                       (first ? n0 : n0 - f) + ct;
-                    *(u32x4*)(out + o) = Vec16<bf16_t>::pack(v);
+                    store_stream(out + o, Vec16<bf16_t>::pack(v));
                 }
             }
         }
