@@ -8,7 +8,9 @@ backward).  The workload is the Mixtral-8x22B-shaped layer: T = 4096 tokens (one
 4096-token sub-sequence), d = 6144, E = 8, top-2, SwiGLU ffn 16384, capacity factor
 1.0, bf16 with fp32 accumulation, seeded synthetic inputs already resident in HBM.
 
-Prints one JSON line.  `roofline` is for the grouped GEMM (the six launches of the
+The timed steps issue the step's launches one by one (`--graph` replays the step
+captured once in a HIP graph instead: the same time, the launches being asynchronous and
+the kernels long); `value` is T over the wall time per step.  Prints one JSON line.  `roofline` is for the grouped GEMM (the six launches of the
 matrix-core GEMM kernel per step, 18 * n_kept * d * f FLOPs), timed with HIP events
 on the stream the kernels run on, with the HBM traffic of those launches taken from
 the hardware-counter summary under profiles/ while the GEMM source is unchanged;
@@ -272,6 +274,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_8x22b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured in a HIP graph instead of the "
+                         "launches issued one by one")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(a known-size reference for hardware byte counters)")
@@ -313,17 +318,33 @@ def main():
     log(f"bench: {args.warmup} warmup steps done")
     n_kept = int(lay.rt["n_kept"].item())
 
-    tm.on = True
+    # --graph: the step's launches are captured once in a HIP graph and the timed steps are
+    # graph replays (the ABI calls allocate nothing and never synchronise, so a step is
+    # capturable).
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_step(lay, inp, L, tm)
+        graph.replay()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run_step(lay, inp, L, tm)
+        if graph is not None:
+            graph.replay()
+        else:
+            run_step(lay, inp, L, tm)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms = dt * 1000.0 / args.steps
+    # per-call HIP events: the same number of steps again, launched one by one
+    tm.on = True
+    for i in range(args.steps):
+        run_step(lay, inp, L, tm)
     calls = tm.means_ms()
-    log(f"bench: {args.steps} timed steps, {ms:.3f} ms/step; per call (ms): "
-        + ", ".join(f"{k} {v:.3f}" for k, v in calls.items()))
+    log(f"bench: {args.steps} timed steps ({'HIP graph replays' if graph else 'eager'}), "
+        f"{ms:.3f} ms/step; per call (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in calls.items()))
 
     T, d, E, K, f, fs = shape.T, shape.d, shape.E, shape.K, shape.f, shape.fs
     gemm_flops = 18.0 * n_kept * d * f + (18.0 * T * d * fs if fs else 0.0)
@@ -358,6 +379,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if shape.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "timing": "HIP graph replay of the whole step" if graph is not None else "eager launches",
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "K": K, "ffn": f,
                    "shared_ffn": fs, "sub_seq": shape.sub_seq, "capacity_factor": shape.cf,
                    "capacity": cap, "n_kept": n_kept, "parallelism": "none (1 GPU)"},
