@@ -17,8 +17,9 @@ constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 4 waves per block
 // Chunks of a row handled by one lane per batch: lane handles chunks c0 + lane + 64u,
 // u < CHUNKS, and issues the loads of a whole batch before using any of them, so that
 // every lane keeps CHUNKS 16-byte loads in flight per source row (rows of d = 6144 bf16
-// are two batches).
-constexpr int CHUNKS = 6;
+// are three batches).  4 measured best (permute 6% faster than 6; 8 and 12 slower, and
+// nontemporal accesses 10-25% slower).
+constexpr int CHUNKS = 4;
 
 // A batch that lies wholly inside the row (FULL) is loaded and stored without per-chunk
 // predicates, so that all its loads issue back to back; the row's last partial batch
