@@ -246,9 +246,10 @@ moe_status moe_route_bwd(const moe_desc* desc, const void* x, const moe_routing*
  *          + dsg_logit_t * w_sg                              (if dsg_logit != NULL)
  *          + dx_add_t                                        (if dx_add != NULL)
  * accumulated in fp32 and stored once.  dxp [R, d]; dlogits [T, E]; w_router [d, E];
- * dsg_logit [T]; w_sg [d]; dx_add [T, d] (e.g. the shared expert's dx); dx_out [T, d];
- * ws of moe_workspace_size(desc, MOE_WS_PERMUTE_BWD) bytes (a transposed copy of the
- * router weight). */
+ * dsg_logit [T]; w_sg [d]; dx_add [T, d] (e.g. the shared expert's dx); dx_out [T, d].
+ * ws of moe_workspace_size(desc, MOE_WS_PERMUTE_BWD) bytes: 0 for E <= 15 (each block
+ * then keeps its slice of the router weight in LDS; ws may be NULL), else a transposed
+ * copy of the router weight, (E + 1) * d elements. */
 moe_status moe_permute_bwd(const moe_desc* desc, const void* dxp, const moe_routing* r,
                            const float* dlogits, const void* w_router, const float* dsg_logit,
                            const void* w_sg, const void* dx_add, void* dx_out, void* ws,

@@ -114,7 +114,9 @@ size_t ws_size(const moe_desc& d, int which) {
             const int64_t ncol8 = (d.E + 1 + 7) / 8 * 8;
             return align256((size_t)chunks * d.d * ncol8 * sizeof(float));
         }
-        case MOE_WS_PERMUTE_BWD: return align256((size_t)(d.E + 1) * d.d * esize(d));
+        case MOE_WS_PERMUTE_BWD:  // a transposed router weight, unless it is staged in LDS
+            return d.E + 1 <= moe::kPermuteBwdSliceCols ? 0
+                                                        : align256((size_t)(d.E + 1) * d.d * esize(d));
         default: return (size_t)-1;
     }
 }

@@ -214,9 +214,11 @@ __global__ void __launch_bounds__(256) transpose_rw_kernel(const T* __restrict__
 }
 
 // dx_t = sum_{kept k} dxp[row_of[t,k]] + sum_k dl[t,e_k] w_rt[e_k] + dz_t w_sg + dx_add_t
-// (terms added in this order)
+// (terms added in this order), one wave per token over its whole row, the router term from
+// the transposed weight rows (L2-resident).  Used for many experts, where a block's slice
+// of the router weight would take too much LDS for the slice kernel below.
 template <typename T>
-__global__ void __launch_bounds__(256) permute_bwd_kernel(
+__global__ void __launch_bounds__(256) permute_bwd_rows_kernel(
     const u32x4* __restrict__ dxp, const int32_t* __restrict__ row_of,
     const uint8_t* __restrict__ keep, const int32_t* __restrict__ topk_idx,
     const float* __restrict__ dlogits, const u32x4* __restrict__ w_rt,
@@ -251,6 +253,148 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
             if (FULL || c < vpr) dx[t * vpr + c] = Vec16<T>::pack(acc[u]);
         }
     });
+}
+
+// dx_t = sum_{kept k} dxp[row_of[t,k]] + sum_k dl[t,e_k] w_router[:,e_k] + dz_t w_sg + dx_add_t
+// (terms added in this order).
+//
+// A block owns one column slice (64 chunks of 16 bytes: lane i holds chunk i of the slice)
+// and a run of tokens.  The slice of the router weight, transposed to [column e][i], and
+// of w_sg sit in LDS, loaded once per block from w_router's own [d, E] layout, so that the
+// router term of every token is an LDS read instead of a row fetched from L2.  A wave
+// reads the routing entries of a window of 64 / KM tokens with one vector load per array
+// (lane j holds slot j % KM of token j / KM) and takes them out with readlane, then walks
+// the window U tokens at a time, issuing the loads of all U tokens' kept dxp pieces (and
+// dx_add pieces) before using any of them.
+//   KM: the largest K the instantiation handles (U * KM = 8 row pieces in flight);
+//   NC: the LDS columns it holds (E, plus w_sg).
+template <typename T, int KM, int NC>
+__global__ void __launch_bounds__(256) permute_bwd_kernel(
+    const u32x4* __restrict__ dxp, const int32_t* __restrict__ row_of,
+    const uint8_t* __restrict__ keep, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ dlogits, const T* __restrict__ w_router,
+    const float* __restrict__ dz, const T* __restrict__ w_sg, const u32x4* __restrict__ dx_add,
+    int ntok, int d, int E, int K, int vpr, int n_slices, int tok_per_block,
+    u32x4* __restrict__ dx) {
+    constexpr int N = Vec16<T>::N;   // elements per chunk
+    constexpr int SW = 64 * N;       // columns of a slice
+    constexpr int U = 8 / KM;        // tokens whose loads are in flight together
+    constexpr int MW = 64 / KM;      // tokens per routing window
+    __shared__ u32x4 wrt[NC * 64];   // [column][lane]: 16 bytes per lane and column
+    T* wrt_e = (T*)wrt;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int slice = blockIdx.x % n_slices;
+    const int i0 = slice * SW;
+    // this lane's chunk of the row; lanes past the row read chunk 0 and store nothing, so
+    // that the wave stays converged for its readlanes
+    const bool live = slice * 64 + lane < vpr;
+    const int c = live ? slice * 64 + lane : 0;
+
+    // router weight slice: element (i, e) of w_router[d][E] -> wrt_e[e * SW + i - i0]
+    if (dlogits) {
+        if ((E % N) == 0) {
+            // 16-byte loads: N consecutive experts of one row i
+            const int per_row = E / N;
+            const u32x4* src = (const u32x4*)(w_router + (int64_t)i0 * E);
+            for (int q = threadIdx.x; q < SW * per_row; q += 256) {
+                const int i = q / per_row, e0 = (q - i * per_row) * N;
+                if (i0 + i < d) {
+                    const u32x4 v = src[q];
+                    const T* pv = (const T*)&v;
+#pragma unroll
+                    for (int j = 0; j < N; ++j) wrt_e[(e0 + j) * SW + i] = pv[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < N; ++j) wrt_e[(e0 + j) * SW + i] = T(0);
+                }
+            }
+        } else {
+            for (int idx = threadIdx.x; idx < SW * E; idx += 256) {
+                const int i = idx / E, e = idx - i * E;
+                wrt_e[e * SW + i] = i0 + i < d ? w_router[(int64_t)(i0 + i) * E + e] : T(0);
+            }
+        }
+    }
+    if (dz) {
+        for (int i = threadIdx.x; i < SW; i += 256) wrt_e[E * SW + i] = i0 + i < d ? w_sg[i0 + i] : T(0);
+    }
+    __syncthreads();
+
+    const int tb = (blockIdx.x / n_slices) * tok_per_block;
+    const int per_wave = (tok_per_block + 3) >> 2;
+    const int w_lo = __builtin_amdgcn_readfirstlane(min(tb + wave * per_wave, ntok));
+    const int w_hi = __builtin_amdgcn_readfirstlane(min(tb + min((wave + 1) * per_wave, tok_per_block), ntok));
+    for (int tw = w_lo; tw < w_hi; tw += MW) {
+        // routing entries of the window: slot k of token tw + lane / KM
+        const int my_t = tw + lane / KM, my_k = lane % KM;
+        const bool slot = my_t < w_hi && my_k < K;
+        const int64_t sk = (int64_t)my_t * K + my_k;
+        const int rv = slot && keep[sk] ? row_of[sk] : -1;
+        float wv = 0.f;
+        int ev = 0;
+        if (dlogits && slot) {
+            ev = topk_idx[sk];
+            wv = dlogits[(int64_t)my_t * E + ev];
+        }
+        const float zv = dz && lane < MW && tw + lane < w_hi ? dz[tw + lane] : 0.f;
+        const int wn = min(MW, w_hi - tw);
+        for (int u0 = 0; u0 < wn; u0 += U) {
+            u32x4 v[U][KM], va[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u0 + u >= wn) break;
+                const int64_t t = tw + u0 + u;
+#pragma unroll
+                for (int k = 0; k < KM; ++k) {
+                    const int row = __builtin_amdgcn_readlane(rv, (u0 + u) * KM + k);
+                    if (row >= 0) v[u][k] = dxp[(int64_t)row * vpr + c];
+                }
+                if (dx_add) va[u] = dx_add[t * vpr + c];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u0 + u >= wn) break;
+                const int64_t t = tw + u0 + u;
+                float acc[N], f[N];
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[i] = 0.f;
+#pragma unroll
+                for (int k = 0; k < KM; ++k) {
+                    const int row = __builtin_amdgcn_readlane(rv, (u0 + u) * KM + k);
+                    if (row >= 0) {
+                        Vec16<T>::unpack(v[u][k], f);
+#pragma unroll
+                        for (int i = 0; i < N; ++i) acc[i] += 1.0f * f[i];
+                    }
+                }
+                if (dlogits) {
+#pragma unroll
+                    for (int k = 0; k < KM; ++k) {
+                        if (k >= K) break;
+                        const int sl = (u0 + u) * KM + k;
+                        const int e = __builtin_amdgcn_readlane(ev, sl);
+                        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), sl));
+                        Vec16<T>::unpack(wrt[e * 64 + lane], f);
+#pragma unroll
+                        for (int i = 0; i < N; ++i) acc[i] += w * f[i];
+                    }
+                }
+                if (dz) {
+                    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), u0 + u));
+                    Vec16<T>::unpack(wrt[E * 64 + lane], f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) acc[i] += w * f[i];
+                }
+                if (dx_add) {
+                    Vec16<T>::unpack(va[u], f);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) acc[i] += 1.0f * f[i];
+                }
+                if (live) dx[t * vpr + c] = Vec16<T>::pack(acc);
+            }
+        }
+    }
 }
 
 // dl for the K chosen experts: g_j (dgate_j - sum_k g_k dgate_k); 0 elsewhere.
@@ -491,27 +635,47 @@ hipError_t launch_permute_bwd(const moe_desc& d, const void* dxp, const moe_rout
                               const float* dlogits, const void* w_router, const float* dz,
                               const void* w_sg, const void* dx_add, void* dx, void* w_rt,
                               hipStream_t s) {
+    if (d.T == 0) return hipSuccess;
     const int esz = d.dtype == MOE_BF16 ? 2 : 4;
     const int vpr = d.d * esz / 16;
-    const int ncol = d.E + 1;
-    const bool need_rt = dlogits || dz;
-    const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
-    const unsigned tb = blocks_for((int64_t)ncol * d.d, 256);
-    if (d.dtype == MOE_BF16) {
-        if (need_rt)
-            transpose_rw_kernel<bf16_t><<<tb, 256, 0, s>>>(
-                (const bf16_t*)w_router, (const bf16_t*)w_sg, (bf16_t*)w_rt, d.d, d.E, ncol);
-        permute_bwd_kernel<bf16_t><<<nb, 256, 0, s>>>(
-            (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
-            (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
-    } else {
-        if (need_rt)
-            transpose_rw_kernel<float><<<tb, 256, 0, s>>>(
-                (const float*)w_router, (const float*)w_sg, (float*)w_rt, d.d, d.E, ncol);
-        permute_bwd_kernel<float><<<nb, 256, 0, s>>>(
-            (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
-            (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
+    const int ncol = d.E + 1;  // router columns and w_sg
+    if (ncol > kPermuteBwdSliceCols) {
+        // many experts: transposed weight rows in the workspace, one wave per token
+        const bool need_rt = dlogits || dz;
+        const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
+        const unsigned tb = blocks_for((int64_t)ncol * d.d, 256);
+        auto go = [&](auto tag) {
+            using T = decltype(tag);
+            if (need_rt)
+                transpose_rw_kernel<T><<<tb, 256, 0, s>>>((const T*)w_router, (const T*)w_sg,
+                                                          (T*)w_rt, d.d, d.E, ncol);
+            permute_bwd_rows_kernel<T><<<nb, 256, 0, s>>>(
+                (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
+                (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
+        };
+        if (d.dtype == MOE_BF16) go(bf16_t{});
+        else go(float{});
+        return hipGetLastError();
     }
+    const int n_slices = (vpr + 63) / 64;
+    const int tpb = 32;  // tokens per block (8 per wave): measured best of 16-256
+    const int64_t nb = (int64_t)n_slices * ((d.T + tpb - 1) / tpb);
+    if (nb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    auto go = [&](auto tag, auto km) {
+        using T = decltype(tag);
+        permute_bwd_kernel<T, decltype(km)::value, kPermuteBwdSliceCols><<<(unsigned)nb, 256, 0, s>>>(
+            (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const T*)w_router, dz,
+            (const T*)w_sg, (const u32x4*)dx_add, d.T, d.d, d.E, d.K, vpr, n_slices, tpb,
+            (u32x4*)dx);
+    };
+    using K2 = std::integral_constant<int, 2>;
+    using K8 = std::integral_constant<int, 8>;
+    auto by_k = [&](auto tag) {
+        if (d.K <= 2) go(tag, K2{});
+        else go(tag, K8{});
+    };
+    if (d.dtype == MOE_BF16) by_k(bf16_t{});
+    else by_k(float{});
     return hipGetLastError();
 }
 
