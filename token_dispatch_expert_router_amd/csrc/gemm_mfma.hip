@@ -141,8 +141,11 @@ __device__ __forceinline__ int swz_mn(int r) { return ((r & 3) << 2) ^ (((r >> 3
 // swz_split(k row).
 __device__ __forceinline__ int swz_split(int r) { return (4 * (r & 3)) ^ (((r >> 3) & 1) << 1); }
 // K-major single-k-step tile [256 rows][32 k] (64-byte rows): physical chunk p of row r
-// holds logical chunk p ^ swz_k(r).
-__device__ __forceinline__ int swz_k(int r) { return (r >> 2) & 3; }
+// holds logical chunk p ^ swz_k(r).  Chosen by measurement (SQ_LDS_BANK_CONFLICT over
+// SQ_LDS_IDX_ACTIVE in the forward passes, whose A operand is the only user): (r >> 1) & 3
+// gives 1.3%; (r >> 2) & 3, r & 3 and ((r >> 2) ^ (r >> 4)) & 3 each spend 40% of the
+// LDS cycles in bank conflicts.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
