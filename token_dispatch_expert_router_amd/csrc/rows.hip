@@ -4,7 +4,8 @@
 // paragraph: permutation gathers each expert's tokens into a contiguous block, the
 // un-permutation restores token order, and the backward pass runs the duals.  These
 // kernels are pure HBM streams: every row is moved with 16-byte vector accesses, one
-// wavefront per token, with a batch of loads in flight per lane and source row.
+// wavefront per token (the permute backward with few experts: one column slice of many
+// tokens per block), with a batch of loads in flight per lane.
 #include <type_traits>
 
 #include "common.h"
