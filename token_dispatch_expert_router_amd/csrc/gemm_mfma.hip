@@ -659,6 +659,50 @@ gg_mfma_kernel(GemmArgs g) {
     const uint32_t wbase = smem_base + wv * (32 * P * 4);
     const int cl = lane & 15;
     const int cq = 4 * (lane >> 4);
+    if constexpr (MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP) {
+        // The weight gradients store bf16(acc) and nothing else, so the accumulators are
+        // rounded before staging: half the LDS bytes of the fp32 band (one 8-byte write per
+        // 16x16 block and lane, one 16-byte read per 8-column chunk).  No MFMA overlaps
+        // this epilogue, so its LDS time is part of the pass.
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+        // band row pitch in bf16 elements; measured against 80 and 136 (bank conflicts
+        // 10.0%, 22.9%, 12.9% of the LDS cycles)
+        constexpr int PB = 72;
+        const uint32_t bbase = smem_base + wv * (32 * PB * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4_t& a4 = acc[2 * i + h][j];
+                    const u32x2_t v = {pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3])};
+                    *(lds_u32x2*)(uintptr_t)(bbase + ((16 * h + cl) * PB + 16 * j + cq) * 2) = v;
+                }
+            const int row_base = wm * 128 + i * 32;  // within the block tile
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int q = lane + 64 * t;
+                const int rl = q >> 3, cc = q & 7;
+                const u32x4_t w = *(const lds_u32x4*)(uintptr_t)(bbase + (rl * PB + cc * 8) * 2);
+                const u32x4 v = {w[0], w[1], w[2], w[3]};
+                const int rt = row_base + rl;     // row within the block tile
+                const int ct = wn * 64 + cc * 8;  // column within the block tile
+                if (MODE == GG_WGRAD_DOWN) {
+                    const int64_t o = (int64_t)e * f * d + (int64_t)(m0 + rt) * d + n0 + ct;
+                    store_stream((bf16_t*)g.C0 + o, v);
+                } else {
+                    const bool first = n0 < f;
+                    bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
+                    const int64_t o = (int64_t)e * d * f + (int64_t)(m0 + rt) * f +
+                                      (first ? n0 : n0 - f) + ct;
+                    store_stream(out + o, v);
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         if constexpr (MODE == GG_DGRAD_DOWN) {
