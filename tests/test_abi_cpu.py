@@ -64,6 +64,19 @@ def test_max_rows_and_workspace(L):
     assert L.moe_workspace_size(d, L.MOE_WS_FFN_BWD) >= 2 * 512 * 128 * 4
 
 
+@pytest.mark.parametrize("E,dtype,esz", [(1, "MOE_F32", 4), (8, "MOE_BF16", 2), (15, "MOE_BF16", 2),
+                                         (16, "MOE_BF16", 2), (64, "MOE_BF16", 2), (64, "MOE_F32", 4)])
+def test_permute_bwd_workspace(L, E, dtype, esz):
+    # up to 15 experts a block keeps its slice of the router weight in LDS (no workspace);
+    # from 16 on the library writes a transposed copy, (E + 1) * d elements
+    d = L.make_desc(512, 6144, E, 1, 2048, 512, -1, getattr(L, dtype))
+    n = L.moe_workspace_size(d, L.MOE_WS_PERMUTE_BWD)
+    if E + 1 <= 16:
+        assert n == 0
+    else:
+        assert n >= (E + 1) * 6144 * esz and n % 256 == 0
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("K", 9, -1), ("K", 0, -1), ("E", 65, -2), ("E", 0, -2), ("d", 12, -2), ("f", 0, -1),
     ("sub_seq", 100, -1), ("capacity", -2, -1), ("dtype", 7, -2), ("T", -1, -1),
