@@ -289,7 +289,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's MoE layer; --gpus {args.gpus} is not supported "
-              "(the cross-GPU exchanges are not part of this build)", file=sys.stderr)
+              "(the cross-GPU exchanges are outside this library)", file=sys.stderr)
         sys.exit(2)
 
     if args.shard:

@@ -57,7 +57,7 @@ extern "C" {
 typedef int32_t moe_status;
 #define MOE_OK 0
 #define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad size, K > E, T % S != 0, ... */
-#define MOE_ERR_UNSUPPORTED (-2) /* a dtype or shape this build does not handle */
+#define MOE_ERR_UNSUPPORTED (-2) /* a dtype or shape the library does not handle */
 #define MOE_ERR_WORKSPACE (-3)   /* workspace smaller than moe_workspace_size() */
 #define MOE_ERR_HIP (-4)         /* a HIP launch failed; see moe_last_error() */
 
