@@ -35,11 +35,11 @@
 // applied by choosing which global chunk each lane fetches, since a direct load
 // writes its 64 lanes' 16 bytes to 1 KB of consecutive LDS.
 //
-// Staging.  Passes with an M- or N-major operand use a 4-stage ring of single k-steps
-// (32 KB each, three k-steps in flight).  The two dgrad passes, whose operands are both
-// K-major, load pairs of k-steps into two 64 KB slots instead, so that a K-major row
-// is 128 bytes and every load instruction reads whole cache lines (a single k-step
-// would use half of each line it touches, halving the load path's throughput).
+// Staging.  Five passes use a 4-stage ring of single k-steps (32 KB each, three k-steps
+// in flight).  The gate/up dgrad, whose operands are both K-major with 32 KB rows, loads
+// pairs of k-steps into two 64 KB slots instead, so that a K-major row is 128 bytes and
+// every load instruction reads whole cache lines: with single k-steps it ran 24% slower.
+// The down dgrad (both operands K-major, 12 KB rows) runs 3.5% faster on the ring.
 //
 // Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
 // the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
@@ -220,10 +220,10 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
 template <int MODE> struct Traits {
     static constexpr bool a_mn = MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP;
     static constexpr bool b_mn = MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || a_mn;
-    // Both operands K-major: load pairs of k-steps so that every direct-load instruction
-    // reads whole 128-byte lines (a K-major k-step row is only 64 bytes); the other
-    // passes keep the deeper single-k-step ring.
-    static constexpr bool paired = !a_mn && !b_mn;
+    // The gate/up dgrad loads pairs of k-steps so that every direct-load instruction reads
+    // whole 128-byte lines of its 32 KB-pitch rows (a K-major k-step row is only 64
+    // bytes); every other pass keeps the deeper single-k-step ring (measured per pass).
+    static constexpr bool paired = MODE == GG_DGRAD_GATEUP;
 };
 
 // Buffer resource over the raw byte range [base, base + bytes): a direct load through it
@@ -342,28 +342,26 @@ gg_mfma_kernel(GemmArgs g) {
     if constexpr (MODE == GG_DGRAD_DOWN) load_x(0, 0);
 
     if constexpr (TR::paired) {
-        static_assert(!TR::a_mn && !TR::b_mn, "the paired staging holds two K-major operands");
+        static_assert(MODE == GG_DGRAD_GATEUP, "the paired staging serves the gate/up dgrad");
         // ---- direct loads.  K-steps are loaded in pairs (64 k) into two 64 KB slots
         // [A 32 KB | B 32 KB]; group 0 loads A, group 1 loads B, and wave wq of a group issues
         // instructions 8wq .. 8wq+7 of the 32 (1 KB each) that cover one operand of a pair.
         // An operand sits as [256 rows][64 k] with 128-byte rows, so that every instruction
         // reads whole 128-byte lines: instruction ii covers rows 8ii + lane/8, physical chunk
         // lane%8 (swizzle chunk ^ ((row >> 1) & 7)).  Every load goes through a buffer
-        // resource whose base moves with the pair (kbase0 + p * kstride; the gate/up dgrad
-        // switches to kbase1 at k = f) and a fixed per-lane byte offset.
-        const int64_t ld = MODE == GG_DGRAD_DOWN ? d : f;  // row pitch of both operands
-        uint64_t kbase0, kbase1 = 0;
+        // resource whose base moves with the pair (kbase0 + p * kstride, switching to kbase1
+        // at k = f: da with W_g, then db with W_u) and a fixed per-lane byte offset.
+        const int64_t ld = f;  // row pitch of both operands
+        uint64_t kbase0, kbase1;
         if (grp == 0) {
             kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld);
-            if (MODE == GG_DGRAD_GATEUP) kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
-        } else if (MODE == GG_DGRAD_DOWN) {
-            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
+            kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
         } else {
             kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
             kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
         }
         const uint64_t kstride = (uint64_t)KP * 2;
-        const int psplit = MODE == GG_DGRAD_GATEUP ? f / KP : 0x7FFFFFFF;
+        const int psplit = f / KP;
         const int np = (nk + 1) >> 1;
         uint32_t voff[8];
     #pragma unroll
