@@ -35,11 +35,11 @@
 // applied by choosing which global chunk each lane fetches, since a direct load
 // writes its 64 lanes' 16 bytes to 1 KB of consecutive LDS.
 //
-// Staging.  Five passes use a 4-stage ring of single k-steps (32 KB each, three k-steps
-// in flight).  The gate/up dgrad, whose operands are both K-major with 32 KB rows, loads
-// pairs of k-steps into two 64 KB slots instead, so that a K-major row is 128 bytes and
-// every load instruction reads whole cache lines: with single k-steps it ran 24% slower.
-// The down dgrad (both operands K-major, 12 KB rows) runs 3.5% faster on the ring.
+// Staging.  Every pass uses a 4-stage ring of single k-steps (32 KB each, three k-steps
+// in flight), except the gate/up dgrad when its operands' rows (both K-major) are a
+// multiple of 32 KB apart: it then loads pairs of k-steps into two 64 KB slots, so that
+// a K-major row is 128 bytes and every load instruction reads whole cache lines (with
+// single k-steps, 16 rows of 64 bytes 32 KB apart per instruction, it ran 16-31% slower).
 //
 // Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
 // the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
@@ -217,13 +217,16 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
     return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-template <int MODE> struct Traits {
+// PAIRED (gate/up dgrad only): stage pairs of k-steps, so that every direct-load
+// instruction reads whole 128-byte lines (a K-major k-step row is only 64 bytes).  The
+// launch picks it when the operands' row pitch, 2f bytes, is a multiple of 32 KB: there
+// single k-steps (16 rows of 64 bytes per load instruction, rows 32 KB apart) ran 16-31%
+// slower; at every other pitch measured (4, 5, 16, 40, 56 KB) they ran 1-7% faster.
+template <int MODE, bool PAIRED> struct Traits {
     static constexpr bool a_mn = MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP;
     static constexpr bool b_mn = MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || a_mn;
-    // The gate/up dgrad loads pairs of k-steps so that every direct-load instruction reads
-    // whole 128-byte lines of its 32 KB-pitch rows (a K-major k-step row is only 64
-    // bytes); every other pass keeps the deeper single-k-step ring (measured per pass).
-    static constexpr bool paired = MODE == GG_DGRAD_GATEUP;
+    static constexpr bool paired = PAIRED;
+    static_assert(!PAIRED || MODE == GG_DGRAD_GATEUP, "only the gate/up dgrad stages pairs");
 };
 
 // Buffer resource over the raw byte range [base, base + bytes): a direct load through it
@@ -254,12 +257,12 @@ __device__ __forceinline__ void lds_dma16_buf(const i32x4_t& rsrc, uint32_t voff
 // wave of each group.  Block barriers alternate the two roles.
 constexpr int NTHREADS = 512;
 
-template <int MODE>
+template <int MODE, bool PAIRED>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 gg_mfma_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
-    using TR = Traits<MODE>;
+    using TR = Traits<MODE, PAIRED>;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -800,9 +803,9 @@ gg_mfma_kernel(GemmArgs g) {
     }
 }
 
-template <int MODE>
+template <int MODE, bool PAIRED = false>
 hipError_t launch_mode(const GemmArgs& a, unsigned g8, hipStream_t s) {
-    gg_mfma_kernel<MODE><<<g8, NTHREADS, 0, s>>>(a);
+    gg_mfma_kernel<MODE, PAIRED><<<g8, NTHREADS, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -832,7 +835,9 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
         case GG_FWD_GATEUP: return launch_mode<GG_FWD_GATEUP>(a, G, s);
         case GG_FWD_DOWN: return launch_mode<GG_FWD_DOWN>(a, G, s);
         case GG_DGRAD_DOWN: return launch_mode<GG_DGRAD_DOWN>(a, G, s);
-        case GG_DGRAD_GATEUP: return launch_mode<GG_DGRAD_GATEUP>(a, G, s);
+        case GG_DGRAD_GATEUP:
+            return ((int64_t)a.f * 2) % 32768 == 0 ? launch_mode<GG_DGRAD_GATEUP, true>(a, G, s)
+                                                   : launch_mode<GG_DGRAD_GATEUP, false>(a, G, s);
         case GG_WGRAD_DOWN: return launch_mode<GG_WGRAD_DOWN>(a, G, s);
         default: return launch_mode<GG_WGRAD_GATEUP>(a, G, s);
     }
