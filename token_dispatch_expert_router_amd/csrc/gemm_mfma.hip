@@ -650,11 +650,11 @@ gg_mfma_kernel(GemmArgs g) {
     // Epilogue.  The MFMAs take the B fragment as their first operand, so each 16x16
     // block accumulates C transposed: lane holds row (lane & 15) of the block and the
     // four consecutive columns 4*(lane/16) + r, r = 0..3 (one 16-byte LDS write).  Each
-    // wave stages one
-    // 32-row band of its fp32 results (32 x 64) at a time in a private 8.5 KB of LDS,
-    // then every lane handles 8-column chunks: 16-byte loads of epilogue inputs and
-    // 16-byte stores.  Every wave has passed the last barrier after the last reads of
-    // the operand stages, and no direct load is in flight.
+    // wave stages one 32-row band of its results (32 x 64; fp32, or bf16 for the weight
+    // gradients) at a time in a private 8.5 KB of LDS, then every lane handles 8-column
+    // chunks: 16-byte loads of epilogue inputs and 16-byte stores.  Every wave has passed
+    // the last barrier after the last reads of the operand stages, and no direct load is
+    // in flight.
     typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
     constexpr int P = 68;  // band row pitch in floats
     const uint32_t wbase = smem_base + wv * (32 * P * 4);
@@ -788,16 +788,8 @@ gg_mfma_kernel(GemmArgs g) {
                         *(u32x4*)((bf16_t*)g.C0 + o) = Vec16<bf16_t>::pack(dav);
                         *(u32x4*)((bf16_t*)g.C1 + o) = Vec16<bf16_t>::pack(dbv);
                     }
-                } else if (MODE == GG_WGRAD_DOWN) {
-                    const int64_t o = (int64_t)e * f * d + (int64_t)(m0 + rt) * d + n0 + ct;
-                    store_stream((bf16_t*)g.C0 + o, Vec16<bf16_t>::pack(v));
-                } else {  // GG_WGRAD_GATEUP
-                    const bool first = n0 < f;
-                    bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
-                    const int64_t o = (int64_t)e * d * f + (int64_t)(m0 + rt) * f +
-                                      (first ? n0 : n0 - f) + ct;
-                    store_stream(out + o, Vec16<bf16_t>::pack(v));
                 }
+                // (the weight gradients returned from their bf16 staging above)
             }
         }
     }
