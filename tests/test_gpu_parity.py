@@ -87,6 +87,11 @@ CASES = {
     # case here takes the single-k-step ring)
     "paired_dgrad": _shape("paired_dgrad", T=384, d=512, E=2, K=1, f=16384, sub_seq=384, seed=27,
                            w_std=0.02),
+    # the permute backward's two forms at their boundary: E = 15 with a shared expert fills
+    # all 16 LDS columns of the slice kernel (w_sg in the last), E = 16 takes the transposed
+    # router weight; d = 640 leaves the last column slice partly empty
+    "slice_e15": _shape("slice_e15", T=256, d=640, E=15, K=8, f=256, fs=256, seed=28, w_std=0.05),
+    "rows_e16": _shape("rows_e16", T=256, d=640, E=16, K=8, f=256, fs=256, seed=29, w_std=0.05),
 }
 
 
