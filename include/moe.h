@@ -160,6 +160,22 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
                      float* sg_logit_out, const moe_routing* r, void* ws, size_t ws_bytes,
                      void* stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * and results as moe_route without the workspace.  Its scratch (what moe_route keeps
+ * in `ws`) is a fixed array of MOE_ROUTE_SCRATCH_BYTES in the library's device memory,
+ * one copy per GPU, reserved for the life of the process; the call itself allocates
+ * nothing.  A shape whose moe_workspace_size(desc, MOE_WS_ROUTE) exceeds it is
+ * rejected with MOE_ERR_UNSUPPORTED before any launch.  Every call on one GPU uses
+ * that GPU's copy, so calls that overlap in time on one GPU (different streams, or
+ * different host threads) race and must be serialised by the caller; calls on one
+ * stream are ordered and safe.  Nothing of the scratch needs clearing between calls.
+ * The first call on each GPU looks the array's address up on that GPU. */
+#define MOE_ROUTE_SCRATCH_BYTES (16u << 20)
+moe_status moe_route_noalloc(const moe_desc* desc, const void* x, const void* w_router,
+                             const float* bias, const void* w_sg, float* logits_out,
+                             float* sg_logit_out, const moe_routing* r, void* stream);
+
 /* The routing steps of moe_route from given fp32 logits [T, E] (no GEMM).  The
  * decisions are bit-exact functions of the logits: softmax with this library's
  * own exp (Cody-Waite reduction, degree-7 Taylor polynomial), pairwise sums, IEEE

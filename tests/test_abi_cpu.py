@@ -145,3 +145,27 @@ def test_binding_raises_library_error(L):
     with pytest.raises(L.MoeError) as ei:
         L.moe_route_from_logits(uneven, None, L.Routing(), None, stream=s0)
     assert "multiple" in str(ei.value)
+
+
+def test_noalloc_route_rejects_oversize_before_any_launch(L):
+    """moe_route_noalloc works inside a fixed scratch of MOE_ROUTE_SCRATCH_BYTES: a shape
+    whose route workspace is larger is refused with MOE_ERR_UNSUPPORTED (no HIP call is
+    made, so this runs without a GPU); the Mixtral- and G8T8-shaped layers fit."""
+    lib = L.load()
+    fake = L.Routing(*[ctypes.c_void_p(4096 * (i + 1)) for i in range(10)])
+    p = ctypes.c_void_p(4096)
+    big = L.make_desc(65536, 6144, 64, 8, 2048, 65536, 4096, L.MOE_BF16)
+    assert L.moe_workspace_size(big, L.MOE_WS_ROUTE) > L.MOE_ROUTE_SCRATCH_BYTES
+    st = lib.moe_route_noalloc(ctypes.byref(big), p, p, None, None, p, None, ctypes.byref(fake),
+                               None)
+    assert st == -2 and "scratch" in L.moe_last_error()
+    for shape in ((4096, 6144, 8, 2, 16384, 4096, 1024), (4096, 6144, 64, 8, 2048, 4096, 512),
+                  (8192, 8192, 8, 2, 28672, 8192, -1), (16384, 6144, 8, 2, 16384, 16384, 4096)):
+        d = L.make_desc(*shape, L.MOE_BF16)
+        assert L.moe_workspace_size(d, L.MOE_WS_ROUTE) <= L.MOE_ROUTE_SCRATCH_BYTES
+    # argument errors come first, as for moe_route
+    assert lib.moe_route_noalloc(ctypes.byref(big), None, p, None, None, p, None,
+                                 ctypes.byref(fake), None) == -1
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "#define MOE_ROUTE_SCRATCH_BYTES (16u << 20)" in src
+    assert L.MOE_ROUTE_SCRATCH_BYTES == 16 << 20

@@ -23,7 +23,7 @@ MOE_WS_ROUTE, MOE_WS_FFN_FWD, MOE_WS_FFN_BWD, MOE_WS_ROUTE_BWD, MOE_WS_PERMUTE_B
 
 EXPORTS = [
     "moe_abi_version", "moe_last_error", "moe_capacity", "moe_max_rows", "moe_workspace_size",
-    "moe_route", "moe_route_from_logits", "moe_permute", "moe_expert_ffn_fwd", "moe_unpermute",
+    "moe_route", "moe_route_noalloc", "moe_route_from_logits", "moe_permute", "moe_expert_ffn_fwd", "moe_unpermute",
     "moe_unpermute_bwd", "moe_expert_ffn_bwd", "moe_route_bwd", "moe_permute_bwd",
 ]
 
@@ -74,6 +74,7 @@ def load(path: str = LIB_PATH):
     lib.moe_workspace_size.argtypes = [D, i32]
     sigs = {
         "moe_route": [D, vp, vp, vp, vp, vp, vp, R, vp, sz, vp],
+        "moe_route_noalloc": [D, vp, vp, vp, vp, vp, vp, R, vp],
         "moe_route_from_logits": [D, vp, R, vp, sz, vp],
         "moe_permute": [D, vp, R, vp, vp],
         "moe_expert_ffn_fwd": [D, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -156,6 +157,16 @@ def moe_route(desc, x, w_router, bias, w_sg, logits, sg_logit, routing: Routing,
     _check(load().moe_route(ctypes.byref(desc), _p(x), _p(w_router), _p(bias), _p(w_sg),
                             _p(logits), _p(sg_logit), ctypes.byref(routing), _p(ws),
                             ws_bytes(ws), _stream(stream)))
+
+
+def moe_route_noalloc(desc, x, w_router, bias, w_sg, logits, sg_logit, routing: Routing,
+                      stream=None):
+    _check(load().moe_route_noalloc(ctypes.byref(desc), _p(x), _p(w_router), _p(bias), _p(w_sg),
+                                    _p(logits), _p(sg_logit), ctypes.byref(routing),
+                                    _stream(stream)))
+
+
+MOE_ROUTE_SCRATCH_BYTES = 16 << 20
 
 
 def moe_route_from_logits(desc, logits, routing: Routing, ws, stream=None):

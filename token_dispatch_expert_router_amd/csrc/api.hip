@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -157,6 +158,66 @@ moe::GemmArgs gemm_args(const moe_desc& d, const int32_t* offsets) {
     return a;
 }
 
+// Argument checks shared by moe_route and moe_route_noalloc (no HIP call).
+moe_status check_route_args(const moe_desc* desc, const void* x, const void* w_router,
+                            const void* w_sg, const float* logits_out,
+                            const float* sg_logit_out, const moe_routing* r) {
+    moe_status st;
+    if ((st = check_desc(desc)) != MOE_OK) return st;
+    if ((st = check_routing(r, desc->T)) != MOE_OK) return st;
+    if (desc->T == 0) return MOE_OK;
+    REQUIRE(x && w_router && logits_out, MOE_ERR_INVALID_ARG, "x, w_router or logits_out is NULL");
+    REQUIRE(!w_sg || sg_logit_out, MOE_ERR_INVALID_ARG, "w_sg given without sg_logit_out");
+    return MOE_OK;
+}
+
+// The router, softmax/top-K, drop and maps launches of a validated call; `w` is the
+// route workspace (route_layout), unused when T == 0.
+moe_status route_launch(const moe_desc& d, const void* x, const void* w_router, const float* bias,
+                        const void* w_sg, float* logits_out, float* sg_logit_out,
+                        const moe_routing& r, char* w, hipStream_t s) {
+    if (d.T == 0) {
+        zero_counts_kernel<<<1, 128, 0, s>>>(r.kept_counts, r.offsets, r.n_kept, d.E);
+        return hip_status(hipGetLastError(), "moe_route");
+    }
+    const RouteLayout l = route_layout(d);
+    hipError_t e = moe::launch_router_fwd(d, x, w_router, bias, w_sg, logits_out, sg_logit_out,
+                                          r, s, w + l.wrt);
+    if (e != hipSuccess) return hip_status(e, "router");
+    moe::RouteWs rw{(int32_t*)(w + l.kcnt), (int32_t*)(w + l.list)};
+    return hip_status(moe::launch_select_and_maps(d, r, rw, s), "select/maps");
+}
+
+// Route scratch of moe_route_noalloc: one copy per GPU, held until the process ends.
+// Every call on a GPU reuses that GPU's copy (calls that overlap on one GPU race).
+// Nothing in it has to start at zero: the select kernels write every per-group count
+// and the kept lists before the maps kernel reads them, and the transposed router
+// weight is rewritten by each call.
+static __device__ __align__(256) char scratch[MOE_ROUTE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each GPU
+
+// Device address of the current GPU's `scratch` (looked up once per GPU).  The host-side
+// name `scratch` is only a handle for the lookup, never an address to pass to a kernel.
+moe_status scratch_ptr(char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d >= %d", dev,
+            kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_dev[dev] = (char*)p;
+    }
+    *out = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,24 +247,28 @@ moe_status moe_route(const moe_desc* desc, const void* x, const void* w_router,
                      float* sg_logit_out, const moe_routing* r, void* ws, size_t ws_bytes,
                      void* stream) {
     moe_status st;
-    if ((st = check_desc(desc)) != MOE_OK) return st;
-    if ((st = check_routing(r, desc->T)) != MOE_OK) return st;
-    const moe_desc& d = *desc;
-    hipStream_t s = (hipStream_t)stream;
-    if (d.T == 0) {
-        zero_counts_kernel<<<1, 128, 0, s>>>(r->kept_counts, r->offsets, r->n_kept, d.E);
-        return hip_status(hipGetLastError(), "moe_route");
-    }
-    REQUIRE(x && w_router && logits_out, MOE_ERR_INVALID_ARG, "x, w_router or logits_out is NULL");
-    REQUIRE(!w_sg || sg_logit_out, MOE_ERR_INVALID_ARG, "w_sg given without sg_logit_out");
-    if ((st = check_ws(d, MOE_WS_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
-    const RouteLayout l = route_layout(d);
-    char* w = (char*)ws;
-    hipError_t e = moe::launch_router_fwd(d, x, w_router, bias, w_sg, logits_out, sg_logit_out,
-                                          *r, s, w + l.wrt);
-    if (e != hipSuccess) return hip_status(e, "router");
-    moe::RouteWs rw{(int32_t*)(w + l.kcnt), (int32_t*)(w + l.list)};
-    return hip_status(moe::launch_select_and_maps(d, *r, rw, s), "select/maps");
+    if ((st = check_route_args(desc, x, w_router, w_sg, logits_out, sg_logit_out, r)) != MOE_OK)
+        return st;
+    if (desc->T > 0 && (st = check_ws(*desc, MOE_WS_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+    return route_launch(*desc, x, w_router, bias, w_sg, logits_out, sg_logit_out, *r, (char*)ws,
+                        (hipStream_t)stream);
+}
+
+moe_status moe_route_noalloc(const moe_desc* desc, const void* x, const void* w_router,
+                             const float* bias, const void* w_sg, float* logits_out,
+                             float* sg_logit_out, const moe_routing* r, void* stream) {
+    moe_status st;
+    if ((st = check_route_args(desc, x, w_router, w_sg, logits_out, sg_logit_out, r)) != MOE_OK)
+        return st;
+    const size_t need = desc->T > 0 ? ws_size(*desc, MOE_WS_ROUTE) : 0;
+    REQUIRE(need <= MOE_ROUTE_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED,
+            "moe_route_noalloc: this shape needs %zu bytes of route scratch, more than the "
+            "library's fixed %zu (use moe_route with a workspace)",
+            need, (size_t)MOE_ROUTE_SCRATCH_BYTES);
+    char* w = nullptr;
+    if (need > 0 && (st = scratch_ptr(&w)) != MOE_OK) return st;
+    return route_launch(*desc, x, w_router, bias, w_sg, logits_out, sg_logit_out, *r, w,
+                        (hipStream_t)stream);
 }
 
 moe_status moe_route_from_logits(const moe_desc* desc, const float* logits, const moe_routing* r,
