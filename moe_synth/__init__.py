@@ -25,7 +25,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["LayerShape", "SHAPES", "shape_by_name", "make_inputs", "ShardShape", "SHARDS",
+__all__ = ["LayerShape", "SHAPES", "shape_by_name", "make_inputs", "make_router_inputs", "ShardShape", "SHARDS",
            "shard_by_name", "make_source_tokens", "make_shard_weights", "make_shard_grad"]
 
 
@@ -135,6 +135,21 @@ def make_inputs(shape: LayerShape, device="cpu", T: Optional[int] = None,
         out["ws_gate"] = _expert_stack(1, s.d, s.fs, s.seed, _SLOT["ws_gate"], s.w_std, dt, device)
         out["ws_up"] = _expert_stack(1, s.d, s.fs, s.seed, _SLOT["ws_up"], s.w_std, dt, device)
         out["ws_down"] = _expert_stack(1, s.fs, s.d, s.seed, _SLOT["ws_down"], s.w_std, dt, device)
+    return out
+
+
+def make_router_inputs(shape: LayerShape, device="cpu") -> dict:
+    """Only the router's inputs of a layer shape (x, w_router, bias), drawn exactly as
+    make_inputs draws them; the expert weights are not drawn."""
+    s = shape
+    dt = s.torch_dtype
+    out = {"x": _randn((s.T, s.d), s.seed, _SLOT["x"], 1.0, dt, device),
+           "w_router": _randn((s.d, s.E), s.seed, _SLOT["w_router"], s.wr_std, dt, device),
+           "bias": None}
+    if s.zipf_bias:
+        b = torch.tensor([1.5 * math.log(1.0 / (e + 1)) for e in range(s.E)],
+                         dtype=torch.float64).to(torch.float32)
+        out["bias"] = b.to(device)
     return out
 
 

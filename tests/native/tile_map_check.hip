@@ -1,0 +1,124 @@
+// Host-side check of the grouped GEMM's tile maps (csrc/tile_map.h, the same functions
+// the kernels run), over given segment offsets.  For each of the six passes it walks
+// every block of the launch grid and checks:
+//   - row passes: the grid holds every real tile; each block maps to at most one tile,
+//     which lies inside one segment (first row in [lo, hi), tile-aligned from lo, limit
+//     hi) with an n-tile in range; each XCD (block b on XCD b % 8) runs one contiguous
+//     range of logical tiles; every (expert, m-tile, n-tile) is produced exactly once;
+//   - weight gradients: every (expert, m-tile, n-tile) exactly once, and each XCD gets
+//     the same share of every expert's tiles to within one.
+// Usage: tile_map_check E R d f off_0 ... off_E   (prints one line per pass; exit 1 on
+// the first violation).
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <vector>
+
+#include "../../token_dispatch_expert_router_amd/csrc/tile_map.h"
+
+using namespace moe;
+
+static int fail(const char* pass, const char* what, long a, long b, long c) {
+    printf("FAIL %s: %s (%ld, %ld, %ld)\n", pass, what, a, b, c);
+    return 1;
+}
+
+static int check_rows(int mode, const char* name, const std::vector<int32_t>& off, int E, int64_t R,
+                      int d, int f) {
+    const int nt_n = tiles::row_n_tiles(mode, d, f);
+    const int64_t G = tiles::grid_blocks(mode, E, R, d, f);
+    const int valid = tiles::count_row_tiles(off.data(), E) * nt_n;
+    if (G % 8 != 0) return fail(name, "grid not a multiple of 8", G, 0, 0);
+    // every real tile has a block: the largest block index xcd_remap can use
+    const int per = (valid + 7) / 8;
+    if ((int64_t)per * 8 > G && valid > 0) return fail(name, "grid too small", G, valid, per);
+    std::vector<int> seen;
+    std::vector<int64_t> base(E + 1, 0);
+    for (int e = 0; e < E; ++e)
+        base[e + 1] = base[e] + (int64_t)((off[e + 1] - off[e] + tiles::BM - 1) / tiles::BM) * nt_n;
+    seen.assign((size_t)base[E], 0);
+    std::vector<int> lo_L(8, 1 << 30), hi_L(8, -1), n_L(8, 0);
+    for (int64_t b = 0; b < G; ++b) {
+        const int L = tiles::xcd_remap((int)b, valid);
+        if (L < 0) continue;
+        int e, m0, m_lim, nt;
+        if (!tiles::decode_rows(L, off.data(), E, nt_n, e, m0, m_lim, nt))
+            return fail(name, "decode failed for a valid tile", b, L, valid);
+        const int lo = off[e], hi = off[e + 1];
+        if (!(m0 >= lo && m0 < hi)) return fail(name, "first row outside its segment", e, m0, lo);
+        if ((m0 - lo) % tiles::BM) return fail(name, "tile not aligned in its segment", e, m0, lo);
+        if (m_lim != hi || hi > R) return fail(name, "row limit", e, m_lim, hi);
+        if (nt < 0 || nt >= nt_n) return fail(name, "n-tile out of range", e, nt, nt_n);
+        const int x = (int)(b % 8);
+        lo_L[x] = L < lo_L[x] ? L : lo_L[x];
+        hi_L[x] = L > hi_L[x] ? L : hi_L[x];
+        n_L[x]++;
+        const int64_t id = base[e] + (int64_t)((m0 - lo) / tiles::BM) * nt_n + nt;
+        if (++seen[(size_t)id] != 1) return fail(name, "tile produced twice", e, m0, nt);
+    }
+    for (size_t i = 0; i < seen.size(); ++i)
+        if (seen[i] != 1) return fail(name, "tile never produced", (long)i, (long)seen.size(), 0);
+    for (int x = 0; x < 8; ++x)
+        if (n_L[x] && hi_L[x] - lo_L[x] + 1 != n_L[x])
+            return fail(name, "an XCD's tiles are not one contiguous range", x, lo_L[x], hi_L[x]);
+    printf("%s blocks %lld tiles %d ok\n", name, (long long)G, valid);
+    return 0;
+}
+
+static int check_wgrad(int mode, const char* name, int E, int64_t R, int d, int f) {
+    int MT, NT;
+    tiles::wgrad_dims(mode, d, f, MT, NT);
+    const int64_t G = tiles::grid_blocks(mode, E, R, d, f);
+    std::vector<int> seen((size_t)E * MT * NT, 0);
+    std::vector<int> share((size_t)E * 8, 0);
+    for (int64_t b = 0; b < G; ++b) {
+        int e, mi, ni;
+        if (!tiles::wgrad_tile((int)b, E, MT, NT, e, mi, ni)) continue;
+        if (e < 0 || e >= E || mi < 0 || mi >= MT || ni < 0 || ni >= NT)
+            return fail(name, "tile out of range", e, mi, ni);
+        if (++seen[((size_t)e * MT + mi) * NT + ni] != 1)
+            return fail(name, "tile produced twice", e, mi, ni);
+        share[(size_t)e * 8 + b % 8]++;
+    }
+    for (size_t i = 0; i < seen.size(); ++i)
+        if (seen[i] != 1) return fail(name, "tile never produced", (long)i, 0, 0);
+    for (int e = 0; e < E; ++e) {
+        int mn = 1 << 30, mx = 0;
+        for (int x = 0; x < 8; ++x) {
+            const int v = share[(size_t)e * 8 + x];
+            mn = v < mn ? v : mn;
+            mx = v > mx ? v : mx;
+        }
+        if (mx - mn > 1) return fail(name, "uneven XCD share of an expert", e, mn, mx);
+    }
+    printf("%s blocks %lld tiles %d ok\n", name, (long long)G, E * MT * NT);
+    return 0;
+}
+
+int main(int argc, char** argv) {
+    if (argc < 6) {
+        fprintf(stderr, "usage: %s E R d f off_0 ... off_E\n", argv[0]);
+        return 2;
+    }
+    const int E = atoi(argv[1]);
+    const int64_t R = atoll(argv[2]);
+    const int d = atoi(argv[3]), f = atoi(argv[4]);
+    if (E < 1 || argc != 5 + E + 1 || d % 256 || f % 256) {
+        fprintf(stderr, "bad arguments\n");
+        return 2;
+    }
+    std::vector<int32_t> off(E + 1);
+    for (int i = 0; i <= E; ++i) off[i] = atoi(argv[5 + i]);
+    if (off[0] != 0) return fail("input", "offsets[0] != 0", off[0], 0, 0);
+    for (int i = 0; i < E; ++i)
+        if (off[i + 1] < off[i]) return fail("input", "offsets decrease", i, off[i], off[i + 1]);
+    if (off[E] > R) return fail("input", "offsets[E] > R", off[E], R, 0);
+    int rc = 0;
+    rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f);
+    rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f);
+    rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f);
+    rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f);
+    rc |= check_wgrad(GG_WGRAD_DOWN, "wgrad_down", E, R, d, f);
+    rc |= check_wgrad(GG_WGRAD_GATEUP, "wgrad_gateup", E, R, d, f);
+    return rc;
+}

@@ -41,6 +41,23 @@ def _compile(src: str) -> str:
     return obj
 
 
+TILE_MAP_CHECK_SRC = os.path.join(ROOT, "tests", "native", "tile_map_check.hip")
+TILE_MAP_CHECK = os.path.join(ROOT, "tests", "native", "tile_map_check")
+
+
+def build_tile_map_check(out: str = TILE_MAP_CHECK) -> str:
+    """Host program of the tests: the grouped GEMM's tile maps (csrc/tile_map.h) compiled
+    for the CPU only, to walk launch grids over given segment offsets."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "-x", "hip", "--cuda-host-only", "-O2", "-std=c++17",
+           "-I", os.path.join(ROOT, "include"), TILE_MAP_CHECK_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on tile_map_check.hip:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libmoe.so; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -52,6 +69,8 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    if os.path.exists(TILE_MAP_CHECK_SRC):
+        build_tile_map_check()
     if verbose:
         print("built", LIB)
     return LIB

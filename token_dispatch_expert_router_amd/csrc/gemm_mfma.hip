@@ -55,6 +55,7 @@
 // weight-gradient passes, whose tiles' K is their expert's segment length, give each
 // XCD an equal contiguous share of every expert instead.
 #include "common.h"
+#include "tile_map.h"
 
 namespace moe {
 namespace {
@@ -78,57 +79,9 @@ constexpr int KP = 2 * BK;                              // k of one pair
 constexpr int OP_BYTES = BM * KP * 2;                   // one operand of one pair: 32 KB
 constexpr int SLOT_BYTES = 2 * OP_BYTES;                // A and B of one pair: 64 KB
 
-// Blocks are dispatched round-robin over the 8 XCDs: block b runs on XCD b & 7.  Logical
-// tile L of `valid` goes to XCD L / ceil(valid / 8), so that each XCD runs a contiguous
-// range of equal length; returns -1 for a block with no tile.
-__device__ __forceinline__ int xcd_remap(int b, int valid) {
-    const int per = (valid + 7) >> 3;
-    const int j = b >> 3;
-    if (j >= per) return -1;
-    const int L = (b & 7) * per + j;
-    return L < valid ? L : -1;
-}
-
-// Row tiles over all segments (the grid is sized for the worst case, ceil(R/256) + E).
-__device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offsets, int E) {
-    int mt = 0;
-    for (int i = 0; i < E; ++i) mt += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
-    return mt;
-}
-
-// Tiles of one segment (or one expert's weight gradient) are ordered in groups of
-// GROUP_M m-tiles, m fastest inside a group, so the ~32 consecutive tiles one XCD runs
-// at a time form a 4 x 8 block that shares 4 row panels and 8 weight panels, however
-// many m-tiles the segment has.
-constexpr int GROUP_M = 4;
-__device__ __forceinline__ void grouped_mn(int loc, int mt, int n_tiles, int& mi, int& ni) {
-    const int gi = loc / (GROUP_M * n_tiles);
-    const int gm = min(GROUP_M, mt - gi * GROUP_M);
-    const int idx = loc - gi * GROUP_M * n_tiles;
-    mi = gi * GROUP_M + idx % gm;
-    ni = idx / gm;
-}
-
-// (expert, m-tile, n-tile) of logical tile L for passes with segmented rows.
-__device__ __forceinline__ bool decode_rows(int L, const int32_t* __restrict__ offsets, int E,
-                                            int n_tiles, int& e, int& m0, int& m_lim, int& nt) {
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-        const int lo = offsets[i], hi = offsets[i + 1];
-        const int mt = (hi - lo + BM - 1) / BM;
-        const int tiles = mt * n_tiles;
-        if (L < acc + tiles) {
-            int mi;
-            grouped_mn(L - acc, mt, n_tiles, mi, nt);
-            e = i;
-            m0 = lo + mi * BM;
-            m_lim = hi;
-            return true;
-        }
-        acc += tiles;
-    }
-    return false;
-}
+using tiles::xcd_remap;
+using tiles::count_row_tiles;
+using tiles::decode_rows;
 
 // Swizzles.  K-major pair tile [256 rows][64 k] (128-byte rows): physical chunk p of
 // row r holds logical chunk p ^ ((r >> 1) & 7); a ds_read_b128 is served 16 consecutive
@@ -274,10 +227,7 @@ gg_mfma_kernel(GemmArgs g) {
     const int d = g.d, f = g.f;
     int e = 0, m0 = 0, m_lim = 0, n0 = 0, k_lo = 0, k_hi = 0, nk = 0;
     if (MODE <= GG_DGRAD_GATEUP) {
-        const int n_tiles = MODE == GG_FWD_GATEUP ? f / 128
-                          : MODE == GG_FWD_DOWN ? d / BN
-                          : MODE == GG_DGRAD_DOWN ? f / BN
-                          : d / BN;
+        const int n_tiles = tiles::row_n_tiles(MODE, d, f);
         // only the tiles the segments have are spread over the XCDs
         const int L = xcd_remap(blockIdx.x, count_row_tiles(g.offsets, g.E) * n_tiles);
         if (L < 0) return;
@@ -288,23 +238,11 @@ gg_mfma_kernel(GemmArgs g) {
                     : MODE == GG_DGRAD_DOWN ? d : 2 * f;
         nk = K / BK;
     } else {
-        // Weight gradients: a tile's K is its expert's segment, which differs between
-        // experts (up to 15x on skewed routings), so XCD x takes the same contiguous
-        // eighth of every expert's tile order, [x per / 8, (x + 1) per / 8): every XCD
-        // then has the same work whatever the segment lengths.  Block b runs the
-        // (b >> 3)-th tile of its XCD's sequence (expert-major).
-        const int Mo = MODE == GG_WGRAD_DOWN ? f : d;
-        const int No = MODE == GG_WGRAD_DOWN ? d : 2 * f;
-        const int MT = Mo / BM, NTl = No / BN;
-        const int per = MT * NTl;
-        const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-        const int lo = (int)((int64_t)x * per / 8);
-        const int cnt = (int)((int64_t)(x + 1) * per / 8) - lo;
-        if (cnt == 0) return;
-        e = j / cnt;
-        if (e >= g.E) return;
-        int mi, ni;
-        grouped_mn(lo + (j - e * cnt), MT, NTl, mi, ni);
+        // Weight gradients: a tile's K is its expert's segment (tiles::wgrad_tile gives
+        // every XCD the same contiguous share of each expert's tiles).
+        int MT, NTl, mi, ni;
+        tiles::wgrad_dims(MODE, d, f, MT, NTl);
+        if (!tiles::wgrad_tile(blockIdx.x, g.E, MT, NTl, e, mi, ni)) return;
         m0 = mi * BM;
         n0 = ni * BN;
         k_lo = g.offsets[e];
@@ -808,19 +746,8 @@ bool mfma_shape_ok(const moe_desc& d) {
 }
 
 hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
-    int64_t tiles;
-    const int64_t mt_max = (a.R + BM - 1) / BM + a.E;  // row tiles over all segments
-    switch (mode) {
-        case GG_FWD_GATEUP: tiles = mt_max * (a.f / 128); break;
-        case GG_FWD_DOWN: tiles = mt_max * (a.d / BN); break;
-        case GG_DGRAD_DOWN: tiles = mt_max * (a.f / BN); break;
-        case GG_DGRAD_GATEUP: tiles = mt_max * (a.d / BN); break;
-        // weight gradients: every XCD runs ceil(per / 8) tiles of each expert (at most)
-        case GG_WGRAD_DOWN: tiles = (int64_t)a.E * (((int64_t)(a.f / BM) * (a.d / BN) + 7) / 8) * 8; break;
-        default: tiles = (int64_t)a.E * (((int64_t)(a.d / BM) * (2 * a.f / BN) + 7) / 8) * 8; break;
-    }
-    if (tiles <= 0) return hipSuccess;
-    const int64_t g8 = (tiles + 7) / 8 * 8;
+    const int64_t g8 = tiles::grid_blocks(mode, a.E, a.R, a.d, a.f);
+    if (g8 <= 0) return hipSuccess;
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const unsigned G = (unsigned)g8;
     switch (mode) {

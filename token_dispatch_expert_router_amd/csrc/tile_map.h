@@ -1,0 +1,127 @@
+// Tile maps of the grouped GEMM (gemm_mfma.hip): which output tile a block computes,
+// and how many blocks a pass launches.  Compiled into the kernels and, unchanged, into a
+// host program that walks every block of a launch over given segment offsets and checks
+// that each output tile is produced exactly once and inside its segment.
+//
+// The experts' rows are contiguous segments [offsets[e], offsets[e+1]) of the permuted
+// buffer whose sizes live only in device memory, so a block of a row-segmented pass
+// finds its (expert, m-tile, n-tile) from `offsets` itself.  Blocks are dispatched
+// round-robin over the 8 XCDs (block b runs on XCD b & 7); the maps give each XCD a
+// contiguous range of tiles, in which consecutive tiles form 4 x N blocks (groups of
+// four m-tiles, M fastest) whose operand panels stay in that XCD's L2.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+namespace tiles {
+
+constexpr int BM = 256;  // output rows per tile
+constexpr int BN = 256;  // output columns per tile (the gate/up forward: 128 of W_g + 128 of W_u)
+constexpr int GROUP_M = 4;
+constexpr int NXCD = 8;
+
+// Logical tile L of `valid` goes to XCD L / ceil(valid / 8), so that each XCD runs a
+// contiguous range of equal length; returns -1 for a block with no tile.
+__host__ __device__ __forceinline__ int xcd_remap(int b, int valid) {
+    const int per = (valid + NXCD - 1) / NXCD;
+    const int j = b / NXCD;
+    if (j >= per) return -1;
+    const int L = (b % NXCD) * per + j;
+    return L < valid ? L : -1;
+}
+
+// Row tiles over all segments (the grid is sized for the worst case, ceil(R/256) + E).
+__host__ __device__ __forceinline__ int count_row_tiles(const int32_t* offsets, int E) {
+    int mt = 0;
+    for (int i = 0; i < E; ++i) mt += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    return mt;
+}
+
+// Tiles of one segment (or one expert's weight gradient) are ordered in groups of
+// GROUP_M m-tiles, m fastest inside a group, so the ~32 consecutive tiles one XCD runs
+// at a time form a 4 x 8 block that shares 4 row panels and 8 weight panels, however
+// many m-tiles the segment has.
+__host__ __device__ __forceinline__ void grouped_mn(int loc, int mt, int n_tiles, int& mi,
+                                                    int& ni) {
+    const int gi = loc / (GROUP_M * n_tiles);
+    const int rest = mt - gi * GROUP_M;
+    const int gm = rest < GROUP_M ? rest : GROUP_M;
+    const int idx = loc - gi * GROUP_M * n_tiles;
+    mi = gi * GROUP_M + idx % gm;
+    ni = idx / gm;
+}
+
+// (expert, first row, segment end, n-tile) of logical tile L for passes with segmented
+// rows; false past the last tile.
+__host__ __device__ __forceinline__ bool decode_rows(int L, const int32_t* offsets, int E,
+                                                     int n_tiles, int& e, int& m0, int& m_lim,
+                                                     int& nt) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+        const int lo = offsets[i], hi = offsets[i + 1];
+        const int mt = (hi - lo + BM - 1) / BM;
+        const int tiles = mt * n_tiles;
+        if (L < acc + tiles) {
+            int mi;
+            grouped_mn(L - acc, mt, n_tiles, mi, nt);
+            e = i;
+            m0 = lo + mi * BM;
+            m_lim = hi;
+            return true;
+        }
+        acc += tiles;
+    }
+    return false;
+}
+
+// n-tiles of a row-segmented pass (modes GG_FWD_GATEUP .. GG_DGRAD_GATEUP).
+__host__ __device__ __forceinline__ int row_n_tiles(int mode, int d, int f) {
+    return mode == GG_FWD_GATEUP ? f / 128
+         : mode == GG_FWD_DOWN ? d / BN
+         : mode == GG_DGRAD_DOWN ? f / BN
+         : d / BN;
+}
+
+// Weight-gradient output [Mo, No] per expert: dW_d is [f, d]; [dW_g | dW_u] is [d, 2f].
+__host__ __device__ __forceinline__ void wgrad_dims(int mode, int d, int f, int& MT, int& NT) {
+    MT = (mode == GG_WGRAD_DOWN ? f : d) / BM;
+    NT = (mode == GG_WGRAD_DOWN ? d : 2 * f) / BN;
+}
+
+// Weight gradients: a tile's K is its expert's segment, which differs between experts (up
+// to 15x on skewed routings), so XCD x takes the same contiguous eighth of every expert's
+// tile order, [x per / 8, (x + 1) per / 8): every XCD then has the same work whatever the
+// segment lengths.  Block b runs the (b / 8)-th tile of its XCD's sequence (expert-major).
+// False for a block with no tile.
+__host__ __device__ __forceinline__ bool wgrad_tile(int b, int E, int MT, int NT, int& e,
+                                                    int& mi, int& ni) {
+    const int per = MT * NT;
+    const int x = b % NXCD, j = b / NXCD;
+    const int lo = (int)((int64_t)x * per / NXCD);
+    const int cnt = (int)((int64_t)(x + 1) * per / NXCD) - lo;
+    if (cnt == 0) return false;
+    e = j / cnt;
+    if (e >= E) return false;
+    grouped_mn(lo + (j - e * cnt), MT, NT, mi, ni);
+    return true;
+}
+
+// Blocks a pass launches (a multiple of 8): row passes are sized for the worst case of
+// ceil(R / 256) + E m-tiles (the real counts live on the device); the weight gradients
+// for ceil(per / 8) tiles of each expert on every XCD.
+__host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, int f) {
+    int64_t tiles;
+    if (mode == GG_WGRAD_DOWN || mode == GG_WGRAD_GATEUP) {
+        int MT, NT;
+        wgrad_dims(mode, d, f, MT, NT);
+        tiles = (int64_t)E * (((int64_t)MT * NT + NXCD - 1) / NXCD) * NXCD;
+    } else {
+        const int64_t mt_max = (R + BM - 1) / BM + E;
+        tiles = mt_max * row_n_tiles(mode, d, f);
+    }
+    return (tiles + NXCD - 1) / NXCD * NXCD;
+}
+
+}  // namespace tiles
+}  // namespace moe
