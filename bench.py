@@ -14,8 +14,10 @@ the kernels long); `value` is T over the wall time per step.  Prints one JSON li
 matrix-core GEMM kernel per step, 18 * n_kept * d * f FLOPs), timed with HIP events
 on the stream the kernels run on, with the HBM traffic of those launches taken from
 the hardware-counter summary under profiles/ while the GEMM source is unchanged;
-`hbm_kernels` gives the same for the row-movement calls; `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+`hbm_kernels` gives the same for the row-movement calls with cold caches (a 1 GiB read
+before each call; `hbm_kernels_warm` back to back), `cold` the whole step after a 1 GiB
+read; `cpu_baseline` times the CPU oracle on the whole workload (about 30 s on 16
+cores for the Mixtral shape).
 """
 from __future__ import annotations
 
@@ -39,17 +41,22 @@ def log(msg):
 
 
 class Timer:
-    """HIP events around the ABI calls of one step, on the current stream."""
+    """HIP events around the ABI calls of one step, on the current stream.  With `flush`
+    set, a 1 GiB buffer is read before each call (outside its events), so the call starts
+    with cold caches: the 256 MB last-level cache and the L2s hold none of its operands."""
 
-    def __init__(self, torch):
+    def __init__(self, torch, flush=None):
         self.torch = torch
         self.acc = {}
         self.on = False
+        self.flush = flush
 
     def __call__(self, name, fn, *a, **kw):
         if not self.on:
             return fn(*a, **kw)
         t = self.torch
+        if self.flush is not None:
+            self.flush()
         s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         s.record()
         fn(*a, **kw)
@@ -59,6 +66,21 @@ class Timer:
     def means_ms(self):
         self.torch.cuda.synchronize()
         return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.acc.items()}
+
+
+FLUSH_BYTES = 1 << 30
+
+
+def make_flush(torch):
+    """Reads FLUSH_BYTES (four times the 256 MB last-level cache) on the current stream, so
+    that the caches hold only clean lines of this buffer: the next call finds none of its
+    operands cached and inherits no dirty lines to write back (a write-flush would charge
+    the write-back of up to 256 MB of someone else's data to the timed call)."""
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def flush():
+        buf.sum()
+    return flush
 
 
 def run_step(lay, inp, L, tm):
@@ -90,49 +112,102 @@ def run_step(lay, inp, L, tm):
        lay.ws_permute_bwd)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_threads():
+    """Threads for the oracle: the CPUs this process may run on, capped by OMP_NUM_THREADS
+    when it is set (the share of the host a one-GPU job gets)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return n
+
+
 def cpu_baseline(shape, inp, lay, cap):
-    """Time the CPU oracle on a bounded sample: the routing of all T tokens, the row
-    movement of all T tokens, and the expert FFN forward + backward of expert 0's kept
-    rows; the expert part is scaled by E (experts have near-equal loads here)."""
+    """Time the CPU oracle, as it stands, on the whole workload: routing of all T tokens
+    (on the GPU's logits, as the parity tests do), permutation, every expert's SwiGLU FFN
+    forward and backward, un-permutation and its backward, the router backward and the
+    permute backward (oracle.layer_fwd_bwd; numpy float64 with the device's bf16 storage
+    points).  The inputs are copied to host memory before the clock starts."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    K, E, T = shape.K, shape.E, shape.T
+    n = cpu_threads()
+    host = {}
+    for k, v in inp.items():
+        if v is None:
+            host[k] = None
+        else:
+            host[k] = v.float().cpu().numpy()
     logits = lay.buf["logits"].cpu().numpy()
-    t0 = time.perf_counter()
-    r = oracle.route(logits, K, shape.sub_seq, cap)
-    t_route = time.perf_counter() - t0
+    with threadpool_limits(limits=n):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        t0 = time.perf_counter()
+        ref = oracle.layer_fwd_bwd(host, shape.K, shape.sub_seq, cap,
+                                   "bf16" if shape.dtype == "bf16" else "f32", logits=logits)
+        total = time.perf_counter() - t0
+    # the oracle's own output is checked against the GPU's on the way (y and dx)
+    err = {}
+    for k in ("y", "dx"):
+        got = lay.buf[k].float().cpu().numpy().astype(np.float64)
+        exp = np.asarray(ref[k], np.float64)
+        err[k] = float(np.max(np.abs(got - exp)) / max(float(np.max(np.abs(exp))), 1e-30))
+    del ref, host
+    return {"value": round(shape.T / total, 2), "unit": "tokens/s", "cores": int(used),
+            "kind": "oracle",
+            "sample": (f"the whole workload: one forward + backward of the layer, all {shape.T} "
+                       f"tokens and all {shape.E} experts (oracle.layer_fwd_bwd, numpy float64 "
+                       f"with bf16 storage points, routing in C)"),
+            "seconds": round(total, 3), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "gpu_vs_oracle_max_abs_rel": err}
 
-    x = inp["x"].float().cpu().numpy()
-    dy = inp["dy"].float().cpu().numpy()
-    t0 = time.perf_counter()
-    xp = oracle.permute(x, r["src_of"], K)
-    o_stub = xp  # the row movement costs the same whatever the rows hold
-    y = oracle.unpermute(o_stub, r["row_of"], r["topk_gate"], r["keep"], "bf16")
-    ub = oracle.unpermute_bwd(dy, o_stub, r["row_of"], r["topk_gate"], r["keep"], r["n_kept"],
-                              "bf16")
-    dx = oracle.permute_bwd(ub["d_o"], r["row_of"], r["keep"], T, "bf16")
-    t_rows = time.perf_counter() - t0
-    del y, dx
 
-    lo, hi = int(r["offsets"][0]), int(r["offsets"][1])
-    wg = inp["w_gate"][0:1].float().cpu().numpy()
-    wu = inp["w_up"][0:1].float().cpu().numpy()
-    wd = inp["w_down"][0:1].float().cpu().numpy()
-    off = np.array([0, hi - lo])
-    t0 = time.perf_counter()
-    a, b, h, o = oracle.expert_ffn_fwd(xp[lo:hi], wg, wu, wd, off, "bf16")
-    fb = oracle.expert_ffn_bwd(xp[lo:hi], a, b, h, wg, wu, wd, off, ub["d_o"][lo:hi], "bf16")
-    t_exp = time.perf_counter() - t0
-    del fb
-    total = t_route + t_rows + E * t_exp
-    return {"value": T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"routing + row movement of all {T} tokens ({t_route + t_rows:.2f} s) and "
-                       f"the expert FFN fwd+bwd of expert 0's {hi - lo} kept rows "
-                       f"({t_exp:.2f} s), the expert part scaled x{E}"),
-            "seconds": round(total, 3)}
+def input_sha256(inp):
+    """SHA-256 of each input tensor's raw bytes (bf16 or fp32 as stored on the device)."""
+    import hashlib
+    import torch
+    out = {}
+    for k, v in inp.items():
+        if v is None:
+            continue
+        h = hashlib.sha256()
+        flat = v.reshape(-1)
+        step = 1 << 26
+        for i in range(0, flat.numel(), step):
+            c = flat[i:i + step]
+            if c.dtype == torch.bfloat16:
+                c = c.view(torch.int16)
+            h.update(c.cpu().numpy().tobytes())
+        out[k] = h.hexdigest()
+    return out
+
+
+def gpu_info(torch):
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, torch.cuda.current_device()) == 0:
+            info["clock_peak_MHz"] = v.value // 1000   # hipDeviceAttributeClockRate (kHz)
+    except OSError:
+        pass
+    info["torch"] = torch.__version__
+    info["hip"] = getattr(torch.version, "hip", None)
+    return info
 
 
 def gemm_traffic(workload):
@@ -274,6 +349,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="mixtral_8x22b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache leg (a 1 GiB read before each timed call)")
+    ap.add_argument("--no-hash", action="store_true", help="skip the inputs' SHA-256")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured in a HIP graph instead of the "
                          "launches issued one by one")
@@ -346,11 +424,38 @@ def main():
     log(f"bench: {args.steps} timed steps ({'HIP graph replays' if graph else 'eager'}), "
         f"{ms:.3f} ms/step; per call (ms): " + ", ".join(f"{k} {v:.3f}" for k, v in calls.items()))
 
+    # cold caches: the same steps again with a 1 GiB read before every call (per-call
+    # figures) and before every step (whole-step figure)
+    calls_cold, ms_cold = None, None
+    if not args.no_cold:
+        flush = make_flush(torch)
+        tmc = Timer(torch, flush=flush)
+        tmc.on = True
+        for i in range(args.steps):
+            run_step(lay, inp, L, tmc)
+        calls_cold = tmc.means_ms()
+        off = Timer(torch)
+        pairs = []
+        for i in range(args.steps):
+            flush()
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            run_step(lay, inp, L, off)
+            z.record()
+            pairs.append((a, z))
+        torch.cuda.synchronize()
+        ms_cold = sum(a.elapsed_time(z) for a, z in pairs) / len(pairs)
+        log(f"bench: cold caches, {ms_cold:.3f} ms/step; per call (ms): "
+            + ", ".join(f"{k} {v:.3f}" for k, v in calls_cold.items()))
+
     T, d, E, K, f, fs = shape.T, shape.d, shape.E, shape.K, shape.f, shape.fs
     gemm_flops = 18.0 * n_kept * d * f + (18.0 * T * d * fs if fs else 0.0)
     router_flops = 6.0 * T * d * E
-    gemm_ms = calls["ffn_fwd"] + calls["ffn_bwd"] + calls.get("shared_fwd", 0) + calls.get(
-        "shared_bwd", 0)
+
+    def gemm_ms_of(c):
+        return c["ffn_fwd"] + c["ffn_bwd"] + c.get("shared_fwd", 0) + c.get("shared_bwd", 0)
+
+    gemm_ms = gemm_ms_of(calls)
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     traffic = gemm_traffic(shape.name)
     s = 2  # bytes per bf16 element
@@ -360,12 +465,19 @@ def main():
         "unpermute_bwd": (T + 2 * n_kept) * d * s + 12 * T * K,
         "permute_bwd": (n_kept + T) * d * s + 4 * T * K,
     }
-    hbm = {k: {"bytes": v, "ms": round(calls[k], 4),
-               "GBs": round(v / (calls[k] * 1e-3) / 1e9, 1),
-               "frac": round(v / (calls[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-           for k, v in hbm_bytes.items()}
-    hb_tot = sum(hbm_bytes.values())
-    hb_ms = sum(calls[k] for k in hbm_bytes)
+
+    def hbm_of(c, label):
+        per = {k: {"bytes": v, "ms": round(c[k], 4),
+                   "GBs": round(v / (c[k] * 1e-3) / 1e9, 1),
+                   "frac": round(v / (c[k] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+               for k, v in hbm_bytes.items()}
+        tot = sum(hbm_bytes.values())
+        t_ms = sum(c[k] for k in hbm_bytes)
+        return {"caches": label, "bytes": tot, "ms": round(t_ms, 4),
+                "GBs": round(tot / (t_ms * 1e-3) / 1e9, 1),
+                "frac": round(tot / (t_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "calls": per}
+
+    kept = host_list(lay.rt["offsets"])
     rec = {
         "metric": METRIC,
         "value": round(T / (ms * 1e-3), 1),
@@ -382,7 +494,8 @@ def main():
         "timing": "HIP graph replay of the whole step" if graph is not None else "eager launches",
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "K": K, "ffn": f,
                    "shared_ffn": fs, "sub_seq": shape.sub_seq, "capacity_factor": shape.cf,
-                   "capacity": cap, "n_kept": n_kept, "parallelism": "none (1 GPU)"},
+                   "capacity": cap, "n_kept": n_kept, "kept_per_expert": kept,
+                   "parallelism": "none (1 GPU)"},
         "tflops": round((gemm_flops + router_flops) / (ms * 1e-3) / 1e12, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -392,12 +505,23 @@ def main():
                      "kernel": "gg_mfma_kernel (6 launches per step: fwd gate/up, fwd down, "
                                "dgrad down, wgrad down, wgrad gate/up, dgrad gate/up)",
                      "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4)},
-        "hbm_kernels": {"bytes": hb_tot, "ms": round(hb_ms, 4),
-                        "GBs": round(hb_tot / (hb_ms * 1e-3) / 1e9, 1),
-                        "frac": round(hb_tot / (hb_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                        "calls": hbm},
         "calls_ms": {k: round(v, 4) for k, v in calls.items()},
     }
+    if calls_cold is not None:
+        gc = gemm_ms_of(calls_cold)
+        rec["roofline"]["frac_cold"] = round(gemm_flops / (gc * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        rec["hbm_kernels"] = hbm_of(calls_cold, "cold: 1 GiB read before each call")
+        rec["hbm_kernels_warm"] = hbm_of(calls, "warm: calls back to back")
+        rec["cold"] = {"ms_per_step": round(ms_cold, 4),
+                       "tokens_per_s": round(T / (ms_cold * 1e-3), 1),
+                       "how": "1 GiB read before each step, HIP events around the step",
+                       "calls_ms": {k: round(v, 4) for k, v in calls_cold.items()}}
+    else:
+        rec["hbm_kernels"] = hbm_of(calls, "warm: calls back to back")
+    rec["gpu"] = gpu_info(torch)
+    rec["host"] = {"cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    if not args.no_hash:
+        rec["inputs_sha256"] = input_sha256(inp)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -408,7 +532,7 @@ def main():
         rec["calib_copy_bytes"] = n * 4
         del src, dst
     if not args.no_cpu_baseline:
-        log("bench: timing the CPU oracle on a bounded sample")
+        log("bench: timing the CPU oracle on the whole workload")
         rec["cpu_baseline"] = cpu_baseline(shape, inp, lay, cap)
     print(json.dumps(rec), flush=True)
 
