@@ -218,7 +218,8 @@ moe_status moe_unpermute(const moe_desc* desc, const void* o, const moe_routing*
 
 /* ---- backward (loss L with dL/dy = dy) ------------------------------------------- */
 
-/* Dual of moe_unpermute: d_o[row_of[t,k]] = g_tk * dy_t and
+/* Dual of moe_unpermute (method paragraph: the backward pass runs the forward steps'
+ * duals; this is the un-permutation's): d_o[row_of[t,k]] = g_tk * dy_t and
  * dgate[t,k] = <dy_t, o[row_of[t,k]]> (0 for a dropped slot).  With a shared
  * expert: dshared_t = sigmoid(z_t) * dy_t and dsg_logit_t = <dy_t, shared_t> *
  * s_t (1 - s_t).  dy [T, d]; d_o_out [R, d]; dgate_out [T, K] float;
@@ -228,7 +229,8 @@ moe_status moe_unpermute_bwd(const moe_desc* desc, const void* dy, const void* o
                              const float* sg_logit, void* d_o_out, float* dgate_out,
                              void* dshared_out, float* dsg_logit_out, void* stream);
 
-/* Dual of moe_expert_ffn_fwd, per segment e:
+/* Dual of moe_expert_ffn_fwd (method paragraph: the backward pass runs the duals; this
+ * is the expert FFN's), per segment e:
  *   dh = d_o W_d,e^T ; da = dh * b * sig(a) (1 + a (1 - sig(a))) ; db = dh * silu(a)
  *   dW_d,e = h^T d_o ; dW_g,e = xp^T da ; dW_u,e = xp^T db ;
  *   dxp = da W_g,e^T + db W_u,e^T.
@@ -244,7 +246,9 @@ moe_status moe_expert_ffn_bwd(const moe_desc* desc, const void* xp, const void* 
                               void* dw_up_out, void* dw_down_out, void* ws, size_t ws_bytes,
                               void* stream);
 
-/* Router backward.  Gates are the softmax of the K chosen logits, so for the
+/* Router backward (method paragraph: the backward pass runs the duals; this is the
+ * router's, with the Top-K selection and the Section 3.3 drops held fixed).  Gates are
+ * the softmax of the K chosen logits, so for the
  * chosen experts dl_{e_j} = g_j (dgate_j - sum_k g_k dgate_k) and every other
  * logit gets 0 (the selection and the drops are piecewise constant).  Writes
  * dlogits_out [T, E] float and dw_router_out = x^T dl [d, E]; with dsg_logit
@@ -256,7 +260,8 @@ moe_status moe_route_bwd(const moe_desc* desc, const void* x, const moe_routing*
                          void* dw_router_out, void* dw_sg_out, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* Dual of moe_permute plus the router's input gradient:
+/* Dual of moe_permute plus the router's input gradient (method paragraph: the backward
+ * pass runs the duals; this is the permutation's):
  *   dx_t = sum over kept k (ascending) of dxp[row_of[t,k]]
  *          + sum_k dlogits[t, e_tk] * w_router[:, e_tk]     (if dlogits != NULL)
  *          + dsg_logit_t * w_sg                              (if dsg_logit != NULL)

@@ -83,6 +83,9 @@ CASES = {
     # segments of 50-80 rows: one mostly empty row tile per expert
     "short_segments": _shape("short_segments", T=512, d=512, E=16, K=2, f=512, seed=25,
                              w_std=0.05),
+    # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
+    # tile order per segment
+    "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),
     # 2f bytes a multiple of 32 KB: the gate/up dgrad stages pairs of k-steps (every other
     # case here takes the single-k-step ring)
     "paired_dgrad": _shape("paired_dgrad", T=384, d=512, E=2, K=1, f=16384, sub_seq=384, seed=27,

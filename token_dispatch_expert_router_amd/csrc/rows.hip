@@ -23,15 +23,17 @@ constexpr int ROWS_PER_BLOCK = 4;  // one wave per row, 4 waves per block
 constexpr int CHUNKS = 4;
 
 // A batch that lies wholly inside the row (FULL) is loaded and stored without per-chunk
-// predicates, so that all its loads issue back to back; the row's last partial batch
-// checks every chunk.
+// predicates, so that all its loads issue back to back; in the row's last partial batch a
+// chunk past the row reads the row's last chunk instead (a valid address; its value is
+// never stored), so the loads stay unconditional there too and the batch stays in
+// registers.
 template <bool FULL, int U>
 __device__ __forceinline__ void load_batch(const u32x4* __restrict__ row, int c0, int lane, int vpr,
                                            u32x4 (&v)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int c = c0 + lane + 64 * u;
-        if (FULL || c < vpr) v[u] = row[c];
+        v[u] = row[FULL ? c : min(c, vpr - 1)];
     }
 }
 
@@ -65,29 +67,54 @@ __device__ __forceinline__ void add_batch(const u32x4* __restrict__ row, float w
     }
 }
 
+// The routing entries of a wave's token sit one slot per lane (lane k < K holds slot k),
+// read with one vector load per array as the wave starts; a slot's row (-1 when the slot
+// was dropped) and gate are then taken out with readlane as wave-uniform values, so that
+// the row loads of every slot of a batch can be issued together instead of each waiting
+// for its own routing entry.
+__device__ __forceinline__ int lane_slot_row(const int32_t* __restrict__ row_of, int64_t t, int K,
+                                             int lane) {
+    return lane < K ? row_of[t * K + lane] : -1;
+}
+__device__ __forceinline__ float lane_slot_gate(const float* __restrict__ gate, int64_t t, int K,
+                                                int lane) {
+    return lane < K ? gate[t * K + lane] : 0.f;
+}
+__device__ __forceinline__ int slot_of(int v, int k) { return __builtin_amdgcn_readlane(v, k); }
+__device__ __forceinline__ float slot_of(float v, int k) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+// Chunks per lane per batch of the one-token-per-wave kernels, by the most slots a token
+// has (KM): every batch keeps KM * C (+ dy or shared) 16-byte loads per lane in flight.
+template <int KM> struct RowBatch { static constexpr int C = KM <= 2 ? 6 : KM <= 4 ? 3 : 2; };
+
 // xp[row_of[t,k]] = x[t] for every kept slot (t, k): token-major, so that each row of x
 // is read once and stored to its kept rows (the same xp as gathering xp[r] =
-// x[src_of[r] / K] row by row, with half the reads at K = 2).
+// x[src_of[r] / K] row by row, with half the reads at K = 2).  The loads of x do not wait
+// for the routing entries.
+template <int KM>
 __global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ x,
-                                                      const int32_t* __restrict__ row_of,
-                                                      const uint8_t* __restrict__ keep, int ntok,
+                                                      const int32_t* __restrict__ row_of, int ntok,
                                                       int K, int vpr, u32x4* __restrict__ xp) {
+    constexpr int C = RowBatch<2>::C;
     const int lane = threadIdx.x & 63;
     const int64_t t = wave_token();
     if (t >= ntok) return;
-    int nk = 0;
-    for (int k = 0; k < K; ++k) nk += keep[t * K + k] ? 1 : 0;
-    if (nk == 0) return;
+    const int rv = lane_slot_row(row_of, t, K, lane);
     const u32x4* src = x + t * vpr;
-    for_batches(vpr, [&](int c0, auto full) {
+    for_batches<C>(vpr, [&](int c0, auto full) {
         constexpr bool FULL = decltype(full)::value;
-        u32x4 v[CHUNKS];
+        u32x4 v[C];
         load_batch<FULL>(src, c0, lane, vpr, v);
-        for (int k = 0; k < K; ++k) {
-            if (!keep[t * K + k]) continue;
-            u32x4* dst = xp + (int64_t)row_of[t * K + k] * vpr;
 #pragma unroll
-            for (int u = 0; u < CHUNKS; ++u) {
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            const int row = slot_of(rv, k);
+            if (row < 0) continue;
+            u32x4* dst = xp + (int64_t)row * vpr;
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
                 const int c = c0 + lane + 64 * u;
                 if (FULL || c < vpr) dst[c] = v[u];
             }
@@ -95,33 +122,60 @@ __global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ 
     });
 }
 
-// y_t = sum_{kept k, ascending} g_tk o[row_of[t,k]]  (+ sigmoid(z_t) shared_t)
-template <typename T>
+// y_t = sum_{kept k, ascending} g_tk o[row_of[t,k]]  (+ sigmoid(z_t) shared_t), fp32.
+// Each batch issues the loads of every kept slot (and of the shared row) before adding any.
+template <typename T, int KM>
 __global__ void __launch_bounds__(256) unpermute_kernel(
     const u32x4* __restrict__ o, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, const uint8_t* __restrict__ keep,
-    const u32x4* __restrict__ shared, const float* __restrict__ z, int ntok, int K, int vpr,
-    u32x4* __restrict__ y) {
+    const float* __restrict__ gate, const u32x4* __restrict__ shared, const float* __restrict__ z,
+    int ntok, int K, int vpr, u32x4* __restrict__ y) {
     constexpr int N = Vec16<T>::N;
+    constexpr int C = RowBatch<KM>::C;
     const int lane = threadIdx.x & 63;
     const int64_t t = wave_token();
     if (t >= ntok) return;
+    const int rv = lane_slot_row(row_of, t, K, lane);
+    const float gv = lane_slot_gate(gate, t, K, lane);
     const float s = shared ? sigmoid_f(z[t]) : 0.f;
-    for_batches(vpr, [&](int c0, auto full) {
+    for_batches<C>(vpr, [&](int c0, auto full) {
         constexpr bool FULL = decltype(full)::value;
-        float acc[CHUNKS][N];
+        u32x4 v[KM][C], vs[C];
 #pragma unroll
-        for (int u = 0; u < CHUNKS; ++u)
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            const int row = slot_of(rv, k);
+            if (row >= 0) load_batch<FULL>(o + (int64_t)row * vpr, c0, lane, vpr, v[k]);
+        }
+        if (shared) load_batch<FULL>(shared + t * vpr, c0, lane, vpr, vs);
+        float acc[C][N];
+#pragma unroll
+        for (int u = 0; u < C; ++u)
 #pragma unroll
             for (int i = 0; i < N; ++i) acc[u][i] = 0.f;
-        for (int k = 0; k < K; ++k) {
-            if (!keep[t * K + k]) continue;
-            add_batch<T, FULL>(o + (int64_t)row_of[t * K + k] * vpr, gate[t * K + k], c0, lane, vpr,
-                               acc);
-        }
-        if (shared) add_batch<T, FULL>(shared + t * vpr, s, c0, lane, vpr, acc);
 #pragma unroll
-        for (int u = 0; u < CHUNKS; ++u) {
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            if (slot_of(rv, k) < 0) continue;
+            const float w = slot_of(gv, k);
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                float f[N];
+                Vec16<T>::unpack(v[k][u], f);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[u][i] += w * f[i];
+            }
+        }
+        if (shared) {
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                float f[N];
+                Vec16<T>::unpack(vs[u], f);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[u][i] += s * f[i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
             const int c = c0 + lane + 64 * u;
             if (FULL || c < vpr) y[t * vpr + c] = Vec16<T>::pack(acc[u]);
         }
@@ -130,37 +184,37 @@ __global__ void __launch_bounds__(256) unpermute_kernel(
 
 // d_o[row_of[t,k]] = g_tk dy_t ; dgate_tk = <dy_t, o[row_of[t,k]]> ;
 // shared: dshared_t = s_t dy_t, dz_t = <dy_t, shared_t> s_t (1 - s_t).
-// Each batch of dy is loaded once and used for every kept slot; the slot loop is unrolled
-// to its maximum (8) so that the per-slot dot products stay in registers.
-template <typename T>
+// Each batch loads dy and every kept slot's o piece (and the shared piece) together; the
+// per-slot dot products stay in registers (KM of them).
+template <typename T, int KM>
 __global__ void __launch_bounds__(256) unpermute_bwd_kernel(
     const u32x4* __restrict__ dy, const u32x4* __restrict__ o, const int32_t* __restrict__ row_of,
-    const float* __restrict__ gate, const uint8_t* __restrict__ keep,
-    const u32x4* __restrict__ shared, const float* __restrict__ z, int ntok, int K, int vpr,
-    u32x4* __restrict__ d_o, float* __restrict__ dgate, u32x4* __restrict__ dshared,
-    float* __restrict__ dz) {
+    const float* __restrict__ gate, const u32x4* __restrict__ shared, const float* __restrict__ z,
+    int ntok, int K, int vpr, u32x4* __restrict__ d_o, float* __restrict__ dgate,
+    u32x4* __restrict__ dshared, float* __restrict__ dz) {
     constexpr int N = Vec16<T>::N;
+    constexpr int C = RowBatch<KM>::C;
     const int lane = threadIdx.x & 63;
     const int64_t t = wave_token();
     if (t >= ntok) return;
+    const int rv = lane_slot_row(row_of, t, K, lane);
+    const float gv = lane_slot_gate(gate, t, K, lane);
     const float s = shared ? sigmoid_f(z[t]) : 0.f;
-    float dot[8], sdot = 0.f;
+    float dot[KM], sdot = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dot[k] = 0.f;
-    // one batch: dot += <dy, r>, out = w * dy
-    auto pair = [&](auto full, const u32x4 (&dvr)[CHUNKS], const u32x4* __restrict__ r, float w,
+    for (int k = 0; k < KM; ++k) dot[k] = 0.f;
+    // dot += <dy, r> over one batch; out = w * dy
+    auto pair = [&](auto full, const u32x4 (&dvr)[C], const u32x4 (&rv_)[C], float w,
                     u32x4* __restrict__ out, int c0) -> float {
         constexpr bool FULL = decltype(full)::value;
-        u32x4 rv[CHUNKS];
-        load_batch<FULL>(r, c0, lane, vpr, rv);
         float acc = 0.f;
 #pragma unroll
-        for (int u = 0; u < CHUNKS; ++u) {
+        for (int u = 0; u < C; ++u) {
             const int c = c0 + lane + 64 * u;
             if (!FULL && c >= vpr) continue;
             float dv[N], rf[N], wv[N];
             Vec16<T>::unpack(dvr[u], dv);
-            Vec16<T>::unpack(rv[u], rf);
+            Vec16<T>::unpack(rv_[u], rf);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 acc += dv[i] * rf[i];
@@ -170,23 +224,30 @@ __global__ void __launch_bounds__(256) unpermute_bwd_kernel(
         }
         return acc;
     };
-    for_batches(vpr, [&](int c0, auto full) {
+    for_batches<C>(vpr, [&](int c0, auto full) {
         constexpr bool FULL = decltype(full)::value;
-        u32x4 dvr[CHUNKS];
+        u32x4 dvr[C], v[KM][C], vs[C];
         load_batch<FULL>(dy + t * vpr, c0, lane, vpr, dvr);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < KM; ++k) {
             if (k >= K) break;
-            if (!keep[t * K + k]) continue;
-            const int64_t row = row_of[t * K + k];
-            dot[k] += pair(full, dvr, o + row * vpr, gate[t * K + k], d_o + row * vpr, c0);
+            const int row = slot_of(rv, k);
+            if (row >= 0) load_batch<FULL>(o + (int64_t)row * vpr, c0, lane, vpr, v[k]);
         }
-        if (shared) sdot += pair(full, dvr, shared + t * vpr, s, dshared + t * vpr, c0);
+        if (shared) load_batch<FULL>(shared + t * vpr, c0, lane, vpr, vs);
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            const int row = slot_of(rv, k);
+            if (row < 0) continue;
+            dot[k] += pair(full, dvr, v[k], slot_of(gv, k), d_o + (int64_t)row * vpr, c0);
+        }
+        if (shared) sdot += pair(full, dvr, vs, s, dshared + t * vpr, c0);
     });
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < KM; ++k) {
         if (k >= K) break;
-        const float v = keep[t * K + k] ? wave_sum(dot[k]) : 0.f;
+        const float v = slot_of(rv, k) >= 0 ? wave_sum(dot[k]) : 0.f;
         if (lane == 0) dgate[t * K + k] = v;
     }
     if (shared) {
@@ -217,39 +278,72 @@ __global__ void __launch_bounds__(256) transpose_rw_kernel(const T* __restrict__
 // dx_t = sum_{kept k} dxp[row_of[t,k]] + sum_k dl[t,e_k] w_rt[e_k] + dz_t w_sg + dx_add_t
 // (terms added in this order), one wave per token over its whole row, the router term from
 // the transposed weight rows (L2-resident).  Used for many experts, where a block's slice
-// of the router weight would take too much LDS for the slice kernel below.
-template <typename T>
+// of the router weight would take too much LDS for the slice kernel below.  The token's
+// slots and its dlogits row sit one per lane; each batch issues the loads of every kept
+// dxp piece (and dx_add) together, then those of the K router-weight rows.
+template <typename T, int KM>
 __global__ void __launch_bounds__(256) permute_bwd_rows_kernel(
     const u32x4* __restrict__ dxp, const int32_t* __restrict__ row_of,
-    const uint8_t* __restrict__ keep, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ dlogits, const u32x4* __restrict__ w_rt,
-    const float* __restrict__ dz, const u32x4* __restrict__ dx_add, int ntok, int E, int K,
-    int vpr, u32x4* __restrict__ dx) {
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dlogits,
+    const u32x4* __restrict__ w_rt, const float* __restrict__ dz, const u32x4* __restrict__ dx_add,
+    int ntok, int E, int K, int vpr, u32x4* __restrict__ dx) {
     constexpr int N = Vec16<T>::N;
+    constexpr int C = RowBatch<KM>::C;
     const int lane = threadIdx.x & 63;
     const int64_t t = wave_token();
     if (t >= ntok) return;
-    for_batches(vpr, [&](int c0, auto full) {
+    const int rv = lane_slot_row(row_of, t, K, lane);
+    const int ev = lane < K ? topk_idx[t * K + lane] : 0;
+    const float dl = dlogits && lane < E ? dlogits[t * E + lane] : 0.f;  // lane e: dl[t, e]
+    const float zt = dz ? dz[t] : 0.f;
+    for_batches<C>(vpr, [&](int c0, auto full) {
         constexpr bool FULL = decltype(full)::value;
-        float acc[CHUNKS][N];
+        u32x4 v[KM][C], va[C];
 #pragma unroll
-        for (int u = 0; u < CHUNKS; ++u)
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            const int row = slot_of(rv, k);
+            if (row >= 0) load_batch<FULL>(dxp + (int64_t)row * vpr, c0, lane, vpr, v[k]);
+        }
+        if (dx_add) load_batch<FULL>(dx_add + t * vpr, c0, lane, vpr, va);
+        float acc[C][N];
+#pragma unroll
+        for (int u = 0; u < C; ++u)
 #pragma unroll
             for (int i = 0; i < N; ++i) acc[u][i] = 0.f;
-        for (int k = 0; k < K; ++k) {
-            if (!keep[t * K + k]) continue;
-            add_batch<T, FULL>(dxp + (int64_t)row_of[t * K + k] * vpr, 1.0f, c0, lane, vpr, acc);
+        auto add = [&](const u32x4 (&src)[C], float w) {
+#pragma unroll
+            for (int u = 0; u < C; ++u) {
+                float f[N];
+                Vec16<T>::unpack(src[u], f);
+#pragma unroll
+                for (int i = 0; i < N; ++i) acc[u][i] += w * f[i];
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < KM; ++k) {
+            if (k >= K) break;
+            if (slot_of(rv, k) >= 0) add(v[k], 1.0f);
         }
         if (dlogits) {
-            for (int k = 0; k < K; ++k) {
-                const int e = topk_idx[t * K + k];
-                add_batch<T, FULL>(w_rt + (int64_t)e * vpr, dlogits[t * E + e], c0, lane, vpr, acc);
+#pragma unroll
+            for (int k = 0; k < KM; ++k) {
+                if (k >= K) break;
+                load_batch<FULL>(w_rt + (int64_t)slot_of(ev, k) * vpr, c0, lane, vpr, v[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < KM; ++k) {
+                if (k >= K) break;
+                add(v[k], slot_of(dl, slot_of(ev, k)));
             }
         }
-        if (dz) add_batch<T, FULL>(w_rt + (int64_t)E * vpr, dz[t], c0, lane, vpr, acc);
-        if (dx_add) add_batch<T, FULL>(dx_add + t * vpr, 1.0f, c0, lane, vpr, acc);
+        if (dz) {
+            load_batch<FULL>(w_rt + (int64_t)E * vpr, c0, lane, vpr, v[0]);
+            add(v[0], zt);
+        }
+        if (dx_add) add(va, 1.0f);
 #pragma unroll
-        for (int u = 0; u < CHUNKS; ++u) {
+        for (int u = 0; u < C; ++u) {
             const int c = c0 + lane + 64 * u;
             if (FULL || c < vpr) dx[t * vpr + c] = Vec16<T>::pack(acc[u]);
         }
@@ -292,6 +386,30 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
     const bool live = slice * 64 + lane < vpr;
     const int c = live ? slice * 64 + lane : 0;
 
+    const int tb = (blockIdx.x / n_slices) * tok_per_block;
+    const int per_wave = (tok_per_block + 3) >> 2;
+    const int w_lo = __builtin_amdgcn_readfirstlane(min(tb + wave * per_wave, ntok));
+    const int w_hi = __builtin_amdgcn_readfirstlane(min(tb + min((wave + 1) * per_wave, tok_per_block), ntok));
+    // routing entries of a window: slot k of token tw + lane / KM (row -1 when dropped)
+    int rv = -1, ev = 0;
+    float wv = 0.f, zv = 0.f;
+    auto load_window = [&](int tw) {
+        const int my_t = tw + lane / KM, my_k = lane % KM;
+        const bool slot = my_t < w_hi && my_k < K;
+        const int64_t sk = (int64_t)my_t * K + my_k;
+        rv = slot ? row_of[sk] : -1;
+        ev = 0;
+        wv = 0.f;
+        if (dlogits && slot) {
+            ev = topk_idx[sk];
+            wv = dlogits[(int64_t)my_t * E + ev];
+        }
+        zv = dz && lane < MW && tw + lane < w_hi ? dz[tw + lane] : 0.f;
+    };
+    // the first window's entries are requested before the weight slice is staged, so that
+    // the two loads overlap
+    if (w_lo < w_hi) load_window(w_lo);
+
     // router weight slice: element (i, e) of w_router[d][E] -> wrt_e[e * SW + i - i0]
     if (dlogits) {
         if ((E % N) == 0) {
@@ -322,23 +440,8 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
     }
     __syncthreads();
 
-    const int tb = (blockIdx.x / n_slices) * tok_per_block;
-    const int per_wave = (tok_per_block + 3) >> 2;
-    const int w_lo = __builtin_amdgcn_readfirstlane(min(tb + wave * per_wave, ntok));
-    const int w_hi = __builtin_amdgcn_readfirstlane(min(tb + min((wave + 1) * per_wave, tok_per_block), ntok));
     for (int tw = w_lo; tw < w_hi; tw += MW) {
-        // routing entries of the window: slot k of token tw + lane / KM
-        const int my_t = tw + lane / KM, my_k = lane % KM;
-        const bool slot = my_t < w_hi && my_k < K;
-        const int64_t sk = (int64_t)my_t * K + my_k;
-        const int rv = slot && keep[sk] ? row_of[sk] : -1;
-        float wv = 0.f;
-        int ev = 0;
-        if (dlogits && slot) {
-            ev = topk_idx[sk];
-            wv = dlogits[(int64_t)my_t * E + ev];
-        }
-        const float zv = dz && lane < MW && tw + lane < w_hi ? dz[tw + lane] : 0.f;
+        if (tw != w_lo) load_window(tw);
         const int wn = min(MW, w_hi - tw);
         for (int u0 = 0; u0 < wn; u0 += U) {
             u32x4 v[U][KM], va[U];
@@ -593,10 +696,30 @@ hipError_t launch_permute(const moe_desc& d, int64_t R, const void* x, const moe
                           void* xp, hipStream_t s) {
     const int esz = d.dtype == MOE_BF16 ? 2 : 4;
     const int vpr = d.d * esz / 16;
-    if (R > 0 && d.T > 0)
-        permute_kernel<<<blocks_for(d.T, ROWS_PER_BLOCK), 256, 0, s>>>(
-            (const u32x4*)x, r.row_of, r.keep, d.T, d.K, vpr, (u32x4*)xp);
+    if (R > 0 && d.T > 0) {
+        const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
+        auto go = [&](auto km) {
+            permute_kernel<decltype(km)::value><<<nb, 256, 0, s>>>(
+                (const u32x4*)x, r.row_of, d.T, d.K, vpr, (u32x4*)xp);
+        };
+        if (d.K <= 2) go(std::integral_constant<int, 2>{});
+        else if (d.K <= 4) go(std::integral_constant<int, 4>{});
+        else go(std::integral_constant<int, 8>{});
+    }
     return hipGetLastError();
+}
+
+// Runs go(T{}, std::integral_constant<int, KM>{}) with the element type of the layer and
+// the smallest slot bound KM in {2, 4, 8} that covers K.
+template <typename F>
+void by_dtype_and_slots(const moe_desc& d, F&& go) {
+    auto by_k = [&](auto tag) {
+        if (d.K <= 2) go(tag, std::integral_constant<int, 2>{});
+        else if (d.K <= 4) go(tag, std::integral_constant<int, 4>{});
+        else go(tag, std::integral_constant<int, 8>{});
+    };
+    if (d.dtype == MOE_BF16) by_k(bf16_t{});
+    else by_k(float{});
 }
 
 hipError_t launch_unpermute(const moe_desc& d, const void* o, const moe_routing& r,
@@ -604,14 +727,12 @@ hipError_t launch_unpermute(const moe_desc& d, const void* o, const moe_routing&
     const int esz = d.dtype == MOE_BF16 ? 2 : 4;
     const int vpr = d.d * esz / 16;
     const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
-    if (d.dtype == MOE_BF16)
-        unpermute_kernel<bf16_t><<<nb, 256, 0, s>>>((const u32x4*)o, r.row_of, r.topk_gate, r.keep,
-                                                    (const u32x4*)shared, z, d.T, d.K, vpr,
-                                                    (u32x4*)y);
-    else
-        unpermute_kernel<float><<<nb, 256, 0, s>>>((const u32x4*)o, r.row_of, r.topk_gate, r.keep,
-                                                   (const u32x4*)shared, z, d.T, d.K, vpr,
-                                                   (u32x4*)y);
+    by_dtype_and_slots(d, [&](auto tag, auto km) {
+        using T = decltype(tag);
+        unpermute_kernel<T, decltype(km)::value><<<nb, 256, 0, s>>>(
+            (const u32x4*)o, r.row_of, r.topk_gate, (const u32x4*)shared, z, d.T, d.K, vpr,
+            (u32x4*)y);
+    });
     return hipGetLastError();
 }
 
@@ -621,14 +742,12 @@ hipError_t launch_unpermute_bwd(const moe_desc& d, const void* dy, const void* o
     const int esz = d.dtype == MOE_BF16 ? 2 : 4;
     const int vpr = d.d * esz / 16;
     const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
-    if (d.dtype == MOE_BF16)
-        unpermute_bwd_kernel<bf16_t><<<nb, 256, 0, s>>>(
-            (const u32x4*)dy, (const u32x4*)o, r.row_of, r.topk_gate, r.keep, (const u32x4*)shared,
-            z, d.T, d.K, vpr, (u32x4*)d_o, dgate, (u32x4*)dshared, dz);
-    else
-        unpermute_bwd_kernel<float><<<nb, 256, 0, s>>>(
-            (const u32x4*)dy, (const u32x4*)o, r.row_of, r.topk_gate, r.keep, (const u32x4*)shared,
-            z, d.T, d.K, vpr, (u32x4*)d_o, dgate, (u32x4*)dshared, dz);
+    by_dtype_and_slots(d, [&](auto tag, auto km) {
+        using T = decltype(tag);
+        unpermute_bwd_kernel<T, decltype(km)::value><<<nb, 256, 0, s>>>(
+            (const u32x4*)dy, (const u32x4*)o, r.row_of, r.topk_gate, (const u32x4*)shared, z, d.T,
+            d.K, vpr, (u32x4*)d_o, dgate, (u32x4*)dshared, dz);
+    });
     return hipGetLastError();
 }
 
@@ -645,17 +764,15 @@ hipError_t launch_permute_bwd(const moe_desc& d, const void* dxp, const moe_rout
         const bool need_rt = dlogits || dz;
         const unsigned nb = blocks_for(d.T, ROWS_PER_BLOCK);
         const unsigned tb = blocks_for((int64_t)ncol * d.d, 256);
-        auto go = [&](auto tag) {
+        by_dtype_and_slots(d, [&](auto tag, auto km) {
             using T = decltype(tag);
             if (need_rt)
                 transpose_rw_kernel<T><<<tb, 256, 0, s>>>((const T*)w_router, (const T*)w_sg,
                                                           (T*)w_rt, d.d, d.E, ncol);
-            permute_bwd_rows_kernel<T><<<nb, 256, 0, s>>>(
-                (const u32x4*)dxp, r.row_of, r.keep, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
+            permute_bwd_rows_kernel<T, decltype(km)::value><<<nb, 256, 0, s>>>(
+                (const u32x4*)dxp, r.row_of, r.topk_idx, dlogits, (const u32x4*)w_rt, dz,
                 (const u32x4*)dx_add, d.T, d.E, d.K, vpr, (u32x4*)dx);
-        };
-        if (d.dtype == MOE_BF16) go(bf16_t{});
-        else go(float{});
+        });
         return hipGetLastError();
     }
     const int n_slices = (vpr + 63) / 64;
