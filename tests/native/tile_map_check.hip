@@ -1,9 +1,10 @@
 // Host-side check of the grouped GEMM's tile maps (csrc/tile_map.h, the same functions
 // the kernels run), over given segment offsets.  For each of the six passes it walks
 // every block of the launch grid and checks:
-//   - row passes: the grid holds every real tile; each block maps to at most one tile,
-//     which lies inside one segment (first row in [lo, hi), tile-aligned from lo, limit
-//     hi) with an n-tile in range; each XCD (block b on XCD b % 8) runs one contiguous
+//   - row passes, with and without half-height last tiles: the grid holds every real
+//     tile; each block maps to at most one tile, which lies inside one segment (first row
+//     in [lo, hi), tile-aligned from lo, limit hi, a 128-row tile only as a segment's
+//     last tile reaching its end) with an n-tile in range; each XCD (block b on XCD b % 8) runs one contiguous
 //     range of logical tiles; every (expert, m-tile, n-tile) is produced exactly once;
 //   - weight gradients: every (expert, m-tile, n-tile) exactly once, and each XCD gets
 //     the same share of every expert's tiles to within one.
@@ -24,7 +25,7 @@ static int fail(const char* pass, const char* what, long a, long b, long c) {
 }
 
 static int check_rows(int mode, const char* name, const std::vector<int32_t>& off, int E, int64_t R,
-                      int d, int f) {
+                      int d, int f, bool half) {
     const int nt_n = tiles::row_n_tiles(mode, d, f);
     const int64_t G = tiles::grid_blocks(mode, E, R, d, f);
     const int valid = tiles::count_row_tiles(off.data(), E) * nt_n;
@@ -41,11 +42,15 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
     for (int64_t b = 0; b < G; ++b) {
         const int L = tiles::xcd_remap((int)b, valid);
         if (L < 0) continue;
-        int e, m0, m_lim, nt;
-        if (!tiles::decode_rows(L, off.data(), E, nt_n, e, m0, m_lim, nt))
+        int e, m0, m_lim, nt, mh;
+        if (!tiles::decode_rows(L, off.data(), E, nt_n, half, e, m0, m_lim, nt, mh))
             return fail(name, "decode failed for a valid tile", b, L, valid);
         const int lo = off[e], hi = off[e + 1];
         if (!(m0 >= lo && m0 < hi)) return fail(name, "first row outside its segment", e, m0, lo);
+        // a tile covers rows [m0, min(m0 + mh, hi)); a half-height tile must reach the
+        // segment's end (it is the last one) and only the half-tile launch makes them
+        if (mh != tiles::BM && !(half && mh == tiles::BM / 2 && hi - m0 <= mh))
+            return fail(name, "bad tile height", e, m0, mh);
         if ((m0 - lo) % tiles::BM) return fail(name, "tile not aligned in its segment", e, m0, lo);
         if (m_lim != hi || hi > R) return fail(name, "row limit", e, m_lim, hi);
         if (nt < 0 || nt >= nt_n) return fail(name, "n-tile out of range", e, nt, nt_n);
@@ -61,7 +66,7 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
     for (int x = 0; x < 8; ++x)
         if (n_L[x] && hi_L[x] - lo_L[x] + 1 != n_L[x])
             return fail(name, "an XCD's tiles are not one contiguous range", x, lo_L[x], hi_L[x]);
-    printf("%s blocks %lld tiles %d ok\n", name, (long long)G, valid);
+    printf("%s%s blocks %lld tiles %d ok\n", name, half ? " (half tiles)" : "", (long long)G, valid);
     return 0;
 }
 
@@ -114,10 +119,12 @@ int main(int argc, char** argv) {
         if (off[i + 1] < off[i]) return fail("input", "offsets decrease", i, off[i], off[i + 1]);
     if (off[E] > R) return fail("input", "offsets[E] > R", off[E], R, 0);
     int rc = 0;
-    rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f);
-    rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f);
-    rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f);
-    rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f);
+    for (int h = 0; h < 2; ++h) {
+        rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f, h == 1);
+        rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f, h == 1);
+        rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f, h == 1);
+        rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f, h == 1);
+    }
     rc |= check_wgrad(GG_WGRAD_DOWN, "wgrad_down", E, R, d, f);
     rc |= check_wgrad(GG_WGRAD_GATEUP, "wgrad_gateup", E, R, d, f);
     return rc;

@@ -39,7 +39,7 @@ def _run(exe, offsets, R, d, f):
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     lines = r.stdout.strip().splitlines()
-    assert len(lines) == 6 and all(ln.endswith(" ok") for ln in lines), r.stdout
+    assert len(lines) == 10 and all(ln.endswith(" ok") for ln in lines), r.stdout
     return lines
 
 

@@ -210,55 +210,37 @@ __device__ __forceinline__ void lds_dma16_buf(const i32x4_t& rsrc, uint32_t voff
 // wave of each group.  Block barriers alternate the two roles.
 constexpr int NTHREADS = 512;
 
-template <int MODE, bool PAIRED>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-gg_mfma_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
+// One output tile of BM_ = 32 RB rows (RB = 8: 256 rows; RB = 4: a half-height tile of
+// 128 rows for a segment's last rows) by 256 columns: wave w computes rows
+// 16 RB (w & 1) .. +16 RB - 1 and columns 64 (w >> 1) .. +63 as RB x 4 MFMA blocks.  A
+// half-height tile keeps the full tile's B operand, LDS layout and schedule; its A tile
+// is 128 rows (two direct loads per wave and k-step instead of four) and each compute
+// phase has 16 MFMAs.
+template <int MODE, bool PAIRED, int RB>
+__device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, int e, int m0, int m_lim,
+                                        int n0, int k_lo, int k_hi, int nk) {
+    static_assert(RB == 8 || (RB == 4 && !PAIRED && MODE <= GG_DGRAD_GATEUP),
+                  "half-height tiles serve the row passes on the single-k-step ring");
     using TR = Traits<MODE, PAIRED>;
+    constexpr int WROWS = 16 * RB;  // output rows of a wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = wv >> 2;   // waves w and w + 4 share a SIMD and sit in different groups
     const int wq = wv & 3;     // wave within its group
-    const int wm = wv & 1;     // output rows wm*128 .. +127 of the tile
+    const int wm = wv & 1;     // output rows wm*WROWS .. +WROWS-1 of the tile
     const int wn = wv >> 1;    // output columns wn*64 .. +63 (gate/up: features wn*32 .. +31)
     const int d = g.d, f = g.f;
-    int e = 0, m0 = 0, m_lim = 0, n0 = 0, k_lo = 0, k_hi = 0, nk = 0;
-    if (MODE <= GG_DGRAD_GATEUP) {
-        const int n_tiles = tiles::row_n_tiles(MODE, d, f);
-        // only the tiles the segments have are spread over the XCDs
-        const int L = xcd_remap(blockIdx.x, count_row_tiles(g.offsets, g.E) * n_tiles);
-        if (L < 0) return;
-        int nt;
-        if (!decode_rows(L, g.offsets, g.E, n_tiles, e, m0, m_lim, nt)) return;
-        n0 = nt * (MODE == GG_FWD_GATEUP ? 128 : BN);
-        const int K = MODE == GG_FWD_GATEUP ? d : MODE == GG_FWD_DOWN ? f
-                    : MODE == GG_DGRAD_DOWN ? d : 2 * f;
-        nk = K / BK;
-    } else {
-        // Weight gradients: a tile's K is its expert's segment (tiles::wgrad_tile gives
-        // every XCD the same contiguous share of each expert's tiles).
-        int MT, NTl, mi, ni;
-        tiles::wgrad_dims(MODE, d, f, MT, NTl);
-        if (!tiles::wgrad_tile(blockIdx.x, g.E, MT, NTl, e, mi, ni)) return;
-        m0 = mi * BM;
-        n0 = ni * BN;
-        k_lo = g.offsets[e];
-        k_hi = g.offsets[e + 1];
-        nk = (k_hi - k_lo + BK - 1) / BK;
-    }
 
     const bf16_t* A0 = (const bf16_t*)g.A0;
     const bf16_t* A1 = (const bf16_t*)g.A1;
     const bf16_t* B0 = (const bf16_t*)g.B0;
     const bf16_t* B1 = (const bf16_t*)g.B1;
-    const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
 
-    f32x4_t acc[8][4];
+    f32x4_t acc[RB][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -274,7 +256,7 @@ gg_mfma_kernel(GemmArgs g) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int q = lane + 64 * t;
-            const int row = min(m0 + wm * 128 + i * 32 + (q >> 3), m_lim - 1);
+            const int row = min(m0 + wm * WROWS + i * 32 + (q >> 3), m_lim - 1);
             const int64_t o = (int64_t)row * f + n0 + wn * 64 + (q & 7) * 8;
             xa[buf][t] = *(const u32x4*)((const bf16_t*)g.X0 + o);
             xb[buf][t] = *(const u32x4*)((const bf16_t*)g.X1 + o);
@@ -442,10 +424,14 @@ gg_mfma_kernel(GemmArgs g) {
         }
         const uint64_t kstride = mn ? (uint64_t)BK * ld * 2 : (uint64_t)BK * 2;
         const int ksplit = MODE == GG_DGRAD_GATEUP ? f / BK : nk;
+        // direct loads per wave and k-step: the A tile has 16 RB rows (RB / 2 loads of 16
+        // rows per wave of group 0), the B tile 256 (four per wave of group 1)
+        constexpr int LA = RB / 2;
+        const int nl = grp == 0 ? LA : 4;
         uint32_t voff[4];
     #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int ii = wq * 4 + u;
+            const int ii = wq * (grp == 0 ? LA : 4) + u;
             if (MODE == GG_FWD_GATEUP && grp == 1) {
                 const int kr = 4 * (ii & 7) + (lane >> 4);
                 const int c = (lane & 15) ^ swz_split(kr);
@@ -464,9 +450,9 @@ gg_mfma_kernel(GemmArgs g) {
             }
         }
 
-        // Issue the u-th of this wave's four direct loads of k-step kt into stage st.
+        // Issue the u-th of this wave's nl direct loads of k-step kt into stage st.
         auto issue_one = [&](int kt, int st, int u) {
-            const uint32_t dst = smem_base + st * STEP_STAGE_BYTES + grp * STEP_TILE_BYTES + wq * 4 * 1024 + u * 1024;
+            const uint32_t dst = smem_base + st * STEP_STAGE_BYTES + grp * STEP_TILE_BYTES + (wq * nl + u) * 1024;
             {
                 const bool second = kt >= ksplit;
                 const uint64_t base = (second ? kbase1 : kbase0) +
@@ -483,16 +469,17 @@ gg_mfma_kernel(GemmArgs g) {
         };
         auto issue = [&](int kt, int st) {
     #pragma unroll
-            for (int u = 0; u < 4; ++u) issue_one(kt, st, u);
+            for (int u = 0; u < 4; ++u)
+                if (u < nl) issue_one(kt, st, u);
         };
 
         // Per-lane LDS byte offsets (within a stage) of this wave's fragment reads:
-        // 8 A fragments (16 rows each) and 4 B fragments (16 columns each).
-        uint32_t a_rd[8], b_rd[4];
+        // RB A fragments (16 rows each) and 4 B fragments (16 columns each).
+        uint32_t a_rd[RB], b_rd[4];
     #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            a_rd[i] = TR::a_mn ? addr_mn(0, wm * 128 + i * 16, lane)
-                               : addr_k(0, wm * 128 + i * 16 + (lane & 15), lane >> 4);
+        for (int i = 0; i < RB; ++i)
+            a_rd[i] = TR::a_mn ? addr_mn(0, wm * WROWS + i * 16, lane)
+                               : addr_k(0, wm * WROWS + i * 16 + (lane & 15), lane >> 4);
     #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // gate/up: j = 0, 1 read the W_g sub-tile, j = 2, 3 the W_u sub-tile
@@ -502,11 +489,11 @@ gg_mfma_kernel(GemmArgs g) {
                                : addr_k(STEP_TILE_BYTES, c0 + (lane & 15), lane >> 4);
         }
 
-        Frag<8> fa;
+        Frag<RB> fa;
         Frag<4> fb;
         auto read_stage = [&](uint32_t stage) {
     #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < RB; ++i) {
                 if (TR::a_mn) ds_tr_pair(fa.lo[i], fa.hi[i], stage + a_rd[i]);
                 else ds_b128(fa.q[i], stage + a_rd[i]);
             }
@@ -519,14 +506,24 @@ gg_mfma_kernel(GemmArgs g) {
         };
 
 
+        // Wait until the `pending` newest of this wave's loads at most are in flight (nl per
+        // k-step).
+        auto wait_loads = [&](int pending_ksteps) {
+            if (RB == 8 || nl == 4) {
+                if (pending_ksteps >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                else if (pending_ksteps == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            } else {
+                if (pending_ksteps >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                else if (pending_ksteps == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        };
         // Wait until this wave's loads of k-step kt+1 have landed, leaving the loads of
         // the `ahead` later k-steps that exist in flight.
         auto wait_next = [&](int kt, int ahead) {
             if (kt + 1 >= nk) return;
-            const int newer = min(ahead, nk - 2 - kt);
-            if (newer >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else if (newer == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_loads(min(ahead, nk - 2 - kt));
         };
 
         // Schedule.  Memory phase M(k): read all fragments of k-step k.  Compute phase C(k):
@@ -542,9 +539,7 @@ gg_mfma_kernel(GemmArgs g) {
             issue(0, 0);
             if (nk > 1) issue(1, 1);
             if (nk > 2) issue(2, 2);
-            if (nk > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else if (nk > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_loads(min(nk, 3) - 1);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             if (grp == 1) __builtin_amdgcn_s_barrier();
@@ -563,16 +558,26 @@ gg_mfma_kernel(GemmArgs g) {
                 const bool refill = kt + 3 < nk;
                 const int st3 = (kt + 3) & (STEP_STAGES - 1);
     #pragma unroll
-                for (int q = 0; q < 32; ++q) {
+                for (int q = 0; q < 4 * RB; ++q) {
                     // snake order: consecutive MFMAs differ in one operand only (the
                     // fewest operand changes, which lowers the matrix cores' power)
                     const int i = q >> 2, j = (i & 1) ? 3 - (q & 3) : (q & 3);
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         frag_value<TR::b_mn>(fb, j), frag_value<TR::a_mn>(fa, i), acc[i][j], 0, 0, 0);
-                    if ((q & 7) == 2 && refill) {
-                        __builtin_amdgcn_sched_barrier(0);
-                        issue_one(kt + 3, st3, q >> 3);
-                        __builtin_amdgcn_sched_barrier(0);
+                    // the wave's nl loads spread over the phase: every 8 MFMAs, or every 4
+                    // for the four B loads of a half-height tile's 16 MFMAs
+                    if (RB == 8 || grp == 0) {
+                        if ((q & 7) == 2 && refill) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            issue_one(kt + 3, st3, q >> 3);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+                        if ((q & 3) == 2 && refill) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            issue_one(kt + 3, st3, q >> 2);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                 }
                 __builtin_amdgcn_s_setprio(0);
@@ -610,7 +615,7 @@ gg_mfma_kernel(GemmArgs g) {
         constexpr int PB = 72;
         const uint32_t bbase = smem_base + wv * (32 * PB * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < RB / 2; ++i) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -619,7 +624,7 @@ gg_mfma_kernel(GemmArgs g) {
                     const u32x2_t v = {pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3])};
                     *(lds_u32x2*)(uintptr_t)(bbase + ((16 * h + cl) * PB + 16 * j + cq) * 2) = v;
                 }
-            const int row_base = wm * 128 + i * 32;  // within the block tile
+            const int row_base = wm * WROWS + i * 32;  // within the block tile
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int q = lane + 64 * t;
@@ -643,9 +648,9 @@ gg_mfma_kernel(GemmArgs g) {
         return;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RB / 2; ++i) {
         if constexpr (MODE == GG_DGRAD_DOWN) {
-            if (i + 1 < 4) load_x(i + 1, (i + 1) & 1);
+            if (i + 1 < RB / 2) load_x(i + 1, (i + 1) & 1);
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -657,7 +662,7 @@ gg_mfma_kernel(GemmArgs g) {
                                    __float_as_uint(a4[2]), __float_as_uint(a4[3])};
                 *(lds_u32x4*)(uintptr_t)(wbase + ((16 * h + cl) * P + 16 * j + cq) * 4) = v;
             }
-        const int row_base = wm * 128 + i * 32;  // within the block tile
+        const int row_base = wm * WROWS + i * 32;  // within the block tile
         if (MODE == GG_FWD_GATEUP) {
             // band columns 0..31: a of features wn*32 + 0..31; columns 32..63: b of the same
 #pragma unroll
@@ -733,9 +738,55 @@ gg_mfma_kernel(GemmArgs g) {
     }
 }
 
-template <int MODE, bool PAIRED = false>
+// Row passes (MODE <= GG_DGRAD_GATEUP) find their tile from the segment offsets; with HALF,
+// a segment whose last row tile holds at most 128 rows runs that tile at half height (the
+// tile count is the same).  Weight gradients take tiles::wgrad_tile.
+template <int MODE, bool PAIRED, bool HALF>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+gg_mfma_kernel(GemmArgs g) {
+    static_assert(!HALF || (!PAIRED && MODE <= GG_DGRAD_GATEUP), "half tiles: ring row passes");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
+    const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const int d = g.d, f = g.f;
+    int e = 0, m0 = 0, m_lim = 0, n0 = 0, k_lo = 0, k_hi = 0, nk = 0;
+    bool half = false;
+    if (MODE <= GG_DGRAD_GATEUP) {
+        const int n_tiles = tiles::row_n_tiles(MODE, d, f);
+        // only the tiles the segments have are spread over the XCDs
+        const int L = xcd_remap(blockIdx.x, count_row_tiles(g.offsets, g.E) * n_tiles);
+        if (L < 0) return;
+        int nt, mh;
+        if (!decode_rows(L, g.offsets, g.E, n_tiles, HALF, e, m0, m_lim, nt, mh)) return;
+        half = mh < BM;
+        n0 = nt * (MODE == GG_FWD_GATEUP ? 128 : BN);
+        const int K = MODE == GG_FWD_GATEUP ? d : MODE == GG_FWD_DOWN ? f
+                    : MODE == GG_DGRAD_DOWN ? d : 2 * f;
+        nk = K / BK;
+    } else {
+        // Weight gradients: a tile's K is its expert's segment (tiles::wgrad_tile gives
+        // every XCD the same contiguous share of each expert's tiles).
+        int MT, NTl, mi, ni;
+        tiles::wgrad_dims(MODE, d, f, MT, NTl);
+        if (!tiles::wgrad_tile(blockIdx.x, g.E, MT, NTl, e, mi, ni)) return;
+        m0 = mi * BM;
+        n0 = ni * BN;
+        k_lo = g.offsets[e];
+        k_hi = g.offsets[e + 1];
+        nk = (k_hi - k_lo + BK - 1) / BK;
+    }
+    if constexpr (HALF) {
+        if (half) {
+            gg_tile<MODE, PAIRED, 4>(g, smem_base, e, m0, m_lim, n0, k_lo, k_hi, nk);
+            return;
+        }
+    }
+    gg_tile<MODE, PAIRED, 8>(g, smem_base, e, m0, m_lim, n0, k_lo, k_hi, nk);
+}
+
+template <int MODE, bool PAIRED = false, bool HALF = false>
 hipError_t launch_mode(const GemmArgs& a, unsigned g8, hipStream_t s) {
-    gg_mfma_kernel<MODE, PAIRED><<<g8, NTHREADS, 0, s>>>(a);
+    gg_mfma_kernel<MODE, PAIRED, HALF><<<g8, NTHREADS, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -750,13 +801,24 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
     if (g8 <= 0) return hipSuccess;
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const unsigned G = (unsigned)g8;
+    // Short segments (at most 640 rows per expert by the buffer bound) leave many experts
+    // a last row tile of at most 128 rows: the row passes then take the kernel that runs
+    // such a tile at half height.  Longer segments keep the kernel without that branch.
+    const bool half = (int64_t)a.R <= 640LL * a.E;
     switch (mode) {
-        case GG_FWD_GATEUP: return launch_mode<GG_FWD_GATEUP>(a, G, s);
-        case GG_FWD_DOWN: return launch_mode<GG_FWD_DOWN>(a, G, s);
-        case GG_DGRAD_DOWN: return launch_mode<GG_DGRAD_DOWN>(a, G, s);
+        case GG_FWD_GATEUP:
+            return half ? launch_mode<GG_FWD_GATEUP, false, true>(a, G, s)
+                        : launch_mode<GG_FWD_GATEUP>(a, G, s);
+        case GG_FWD_DOWN:
+            return half ? launch_mode<GG_FWD_DOWN, false, true>(a, G, s)
+                        : launch_mode<GG_FWD_DOWN>(a, G, s);
+        case GG_DGRAD_DOWN:
+            return half ? launch_mode<GG_DGRAD_DOWN, false, true>(a, G, s)
+                        : launch_mode<GG_DGRAD_DOWN>(a, G, s);
         case GG_DGRAD_GATEUP:
-            return ((int64_t)a.f * 2) % 32768 == 0 ? launch_mode<GG_DGRAD_GATEUP, true>(a, G, s)
-                                                   : launch_mode<GG_DGRAD_GATEUP, false>(a, G, s);
+            if (((int64_t)a.f * 2) % 32768 == 0) return launch_mode<GG_DGRAD_GATEUP, true>(a, G, s);
+            return half ? launch_mode<GG_DGRAD_GATEUP, false, true>(a, G, s)
+                        : launch_mode<GG_DGRAD_GATEUP, false>(a, G, s);
         case GG_WGRAD_DOWN: return launch_mode<GG_WGRAD_DOWN>(a, G, s);
         default: return launch_mode<GG_WGRAD_GATEUP>(a, G, s);
     }

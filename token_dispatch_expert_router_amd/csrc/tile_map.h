@@ -52,11 +52,13 @@ __host__ __device__ __forceinline__ void grouped_mn(int loc, int mt, int n_tiles
     ni = idx / gm;
 }
 
-// (expert, first row, segment end, n-tile) of logical tile L for passes with segmented
-// rows; false past the last tile.
+// (expert, first row, segment end, n-tile, tile height) of logical tile L for passes with
+// segmented rows; false past the last tile.  With `half`, a segment's last row tile is
+// 128 rows high when it holds at most 128 rows (the tile count does not change); every
+// other tile is BM rows high.
 __host__ __device__ __forceinline__ bool decode_rows(int L, const int32_t* offsets, int E,
-                                                     int n_tiles, int& e, int& m0, int& m_lim,
-                                                     int& nt) {
+                                                     int n_tiles, bool half, int& e, int& m0,
+                                                     int& m_lim, int& nt, int& mh) {
     int acc = 0;
     for (int i = 0; i < E; ++i) {
         const int lo = offsets[i], hi = offsets[i + 1];
@@ -68,6 +70,7 @@ __host__ __device__ __forceinline__ bool decode_rows(int L, const int32_t* offse
             e = i;
             m0 = lo + mi * BM;
             m_lim = hi;
+            mh = (half && hi - m0 <= BM / 2) ? BM / 2 : BM;
             return true;
         }
         acc += tiles;
