@@ -458,7 +458,7 @@ def main():
     gemm_ms = gemm_ms_of(calls)
     achieved = gemm_flops / (gemm_ms * 1e-3) / 1e12
     traffic = gemm_traffic(shape.name)
-    s = 2  # bytes per bf16 element
+    s = 2 if shape.dtype == "bf16" else 4  # bytes per element
     hbm_bytes = {
         "permute": (T + n_kept) * d * s + 4 * n_kept,
         "unpermute": (n_kept + T) * d * s + 8 * T * K + (T * d * s if fs else 0),
