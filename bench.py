@@ -232,6 +232,24 @@ def gemm_traffic(workload):
     return rec
 
 
+def gemm_passes(workload):
+    """Per-pass averages of the six grouped-GEMM launches from the kernel-trace summary under
+    profiles/ (rocprofv3 --kernel-trace of this bench), while the GEMM source is unchanged."""
+    import hashlib
+    name = "moe_layer_mixtral_8x22b" if workload == "mixtral_8x22b" else workload
+    path = os.path.join(ROOT, "profiles", f"{name}_kernel_trace.md")
+    src = os.path.join(ROOT, "token_dispatch_expert_router_amd", "csrc", "gemm_mfma.hip")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("machine-readable:"):
+            rec = json.loads(line.split(":", 1)[1])
+    if not rec or rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec["passes"]
+
+
 def bench_shard(args):
     """One GPU's expert-side share of the layer spread over G GPUs: the expert FFN
     forward + backward (six grouped-GEMM launches) on the rows its experts receive, with
@@ -504,7 +522,8 @@ def main():
                      "algorithmic_bytes_per_step": (traffic or {}).get("algorithmic_bytes_per_step"),
                      "kernel": "gg_mfma_kernel (6 launches per step: fwd gate/up, fwd down, "
                                "dgrad down, wgrad down, wgrad gate/up, dgrad gate/up)",
-                     "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4)},
+                     "flops_per_step": gemm_flops, "ms_per_step": round(gemm_ms, 4),
+                     "passes_from_kernel_trace": gemm_passes(shape.name)},
         "calls_ms": {k: round(v, 4) for k, v in calls.items()},
     }
     if calls_cold is not None:
