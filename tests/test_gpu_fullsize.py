@@ -349,3 +349,29 @@ def test_fullsize_sampled(name):
                  TOL)
     del lay, inp
     torch.cuda.empty_cache()
+
+
+def test_fullsize_repeat_is_bit_identical():
+    """Two forward + backward steps of the Mixtral-shaped layer on the same inputs give the
+    same bits in every output, gradient and routing array (fixed-order reductions, no
+    atomics on floating-point values)."""
+    s = moe_synth.shape_by_name("mixtral_8x22b")
+    lay, inp, cap = _run_layer(s)
+    first = {k: v.clone() for k, v in lay.buf.items() if isinstance(v, torch.Tensor)}
+    first_rt = {k: v.clone() for k, v in lay.rt.items()}
+    lay.forward_backward(inp)
+    torch.cuda.synchronize()
+    n = int(lay.rt["n_kept"].item())
+    for k, v in first.items():
+        cur = lay.buf[k]
+        if k in ("xp", "a", "b", "h", "o", "d_o", "dxp"):
+            v, cur = v[:n], cur[:n]     # rows past n_kept are not written
+        assert torch.equal(v, cur), f"{k} differs between two identical steps"
+    for k, v in first_rt.items():
+        cur = lay.rt[k]
+        if k == "src_of":
+            v, cur = v[:n], cur[:n]
+        assert torch.equal(v, cur), f"routing {k} differs between two identical steps"
+    log(f"    two steps bit-identical over {len(first)} buffers and {len(first_rt)} routing arrays")
+    del lay, inp, first
+    torch.cuda.empty_cache()

@@ -83,6 +83,15 @@ CASES = {
     # segments of 50-80 rows: one mostly empty row tile per expert
     "short_segments": _shape("short_segments", T=512, d=512, E=16, K=2, f=512, seed=25,
                              w_std=0.05),
+    # slot counts between the kernels' compile-time bounds (2, 4, 8): K = 3 with drops,
+    # K = 5 dropless (8 experts: the permute backward's slice form), K = 6 with 20 experts
+    # (its one-wave-per-token form), and K = 2 with 24 experts (that form's smallest bound)
+    "k3_drop": _shape("k3_drop", T=256, d=256, E=6, K=3, f=256, sub_seq=128, cf=1.0, seed=31,
+                      w_std=0.05),
+    "k5_e8": _shape("k5_e8", T=192, d=256, E=8, K=5, f=256, sub_seq=192, seed=32, w_std=0.05),
+    "k6_e20_drop": _shape("k6_e20_drop", T=128, d=256, E=20, K=6, f=256, sub_seq=64, cf=1.0,
+                          seed=33, w_std=0.05),
+    "k2_e24": _shape("k2_e24", T=256, d=256, E=24, K=2, f=256, seed=34, w_std=0.05),
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
     # tile order per segment
     "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),
@@ -259,3 +268,24 @@ def _random_shapes(n=12, seed=2024):
 def test_random_layer_parity(shape):
     lay, inp, cap = _run(shape)
     check_layer(lay, inp, shape.K, shape.sub_seq, cap, 2e-2)
+
+
+def test_user_stream_matches_default_stream():
+    """The calls take the caller's stream: a layer run on a separate stream gives the same
+    bits as on the current stream."""
+    from token_dispatch_expert_router_amd.layer import MoELayer
+    s = CASES["k3_drop"]
+    inp = moe_synth.make_inputs(s, device="cuda")
+    cap = oracle.capacity(s.sub_seq, s.K, s.E, s.cf)
+    a = MoELayer(s.T, s.d, s.E, s.K, s.f, s.sub_seq, cap, s.torch_dtype, device="cuda")
+    b = MoELayer(s.T, s.d, s.E, s.K, s.f, s.sub_seq, cap, s.torch_dtype, device="cuda")
+    a.forward_backward(inp)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    b.forward_backward(inp, stream=st)
+    st.synchronize()
+    for k in ("y", "dx", "dw_gate", "dw_up", "dw_down", "dw_router", "dlogits"):
+        assert torch.equal(a.buf[k], b.buf[k]), k
+    for k in ("topk_idx", "keep", "row_of", "offsets"):
+        assert torch.equal(a.rt[k], b.rt[k]), k
