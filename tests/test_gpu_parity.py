@@ -92,6 +92,10 @@ CASES = {
     "k6_e20_drop": _shape("k6_e20_drop", T=128, d=256, E=20, K=6, f=256, sub_seq=64, cf=1.0,
                           seed=33, w_std=0.05),
     "k2_e24": _shape("k2_e24", T=256, d=256, E=24, K=2, f=256, seed=34, w_std=0.05),
+    # router GEMM with three 16-column blocks, the 4-wave split of d (d % 256 != 0, five
+    # k-steps per wave: a partial batch) and a last block of 8 tokens
+    "e40_t200": _shape("e40_t200", T=200, d=640, E=40, K=4, f=256, sub_seq=200, seed=35,
+                       w_std=0.05),
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
     # tile order per segment
     "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),

@@ -88,7 +88,6 @@ int64_t max_rows(const moe_desc& d) {
 size_t esize(const moe_desc& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-constexpr int kRouterBwdChunk = 64;   // tokens per partial sum of dW_router
 
 struct RouteLayout {
     size_t kcnt, list, wrt, total;
@@ -111,7 +110,8 @@ size_t ws_size(const moe_desc& d, int which) {
         case MOE_WS_FFN_FWD: return 0;
         case MOE_WS_FFN_BWD: return 2 * align256((size_t)max_rows(d) * d.f * esize(d));
         case MOE_WS_ROUTE_BWD: {
-            const int64_t chunks = (d.T + kRouterBwdChunk - 1) / kRouterBwdChunk;
+            const int chunk = moe::router_bwd_chunk(d.dtype);
+            const int64_t chunks = (d.T + chunk - 1) / chunk;
             const int64_t ncol8 = (d.E + 1 + 7) / 8 * 8;
             return align256((size_t)chunks * d.d * ncol8 * sizeof(float));
         }
@@ -411,10 +411,11 @@ moe_status moe_route_bwd(const moe_desc* desc, const void* x, const moe_routing*
             "x, dgate, dlogits_out or dw_router_out is NULL");
     REQUIRE(!dsg_logit || dw_sg_out, MOE_ERR_INVALID_ARG, "dsg_logit given without dw_sg_out");
     if ((st = check_ws(d, MOE_WS_ROUTE_BWD, ws, ws_bytes)) != MOE_OK) return st;
-    const int chunks = (d.T + kRouterBwdChunk - 1) / kRouterBwdChunk;
+    const int chunk = moe::router_bwd_chunk(d.dtype);
+    const int chunks = (d.T + chunk - 1) / chunk;
     return hip_status(moe::launch_router_bwd(d, x, *r, dgate, dsg_logit, dlogits_out,
                                              dw_router_out, dw_sg_out, (float*)ws, chunks,
-                                             kRouterBwdChunk, (hipStream_t)stream),
+                                             chunk, (hipStream_t)stream),
                       "moe_route_bwd");
 }
 

@@ -122,6 +122,9 @@ hipError_t launch_permute_bwd(const moe_desc& d, const void* dxp, const moe_rout
 // moe_permute_bwd keeps a block's slice of the router weight (E columns and w_sg) in LDS
 // when E + 1 is at most this; more experts use a transposed copy in the workspace.
 constexpr int kPermuteBwdSliceCols = 16;
+// Tokens per partial sum of the router weight gradient (the workspace holds one
+// d x ncol fp32 partial per chunk).
+int router_bwd_chunk(int dtype);
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing& r,
                              const float* dgate, const float* dsg, float* dlogits,
                              void* dw_router, void* dw_sg, float* partial, int n_chunks,

@@ -48,18 +48,95 @@ __device__ __forceinline__ int next_pow2(int v) {
     return p;
 }
 
-// Sum over lanes [0, P) by an xor butterfly (P a power of two): every lane of the
-// group ends with the pairwise-tree sum ((v0+v1)+(v2+v3))+..., the same value on
-// every lane because fp addition is commutative.
+// Cross-lane exchange for the butterflies below, without the LDS crossbar.  Steps 1 and
+// 2 are DPP quad permutations (lane i ^ m); steps 4 and 8 are DPP mirrors within rows of
+// 16 (lane 7 - i within each 8, 15 - i within each 16): that partner lies in the other
+// half of the same group of 2m lanes as i ^ m, so a reduction step combines the same
+// two half-groups.  Steps 16 and 32 use the gfx950 lane swaps across rows and halves
+// (v_permlane16_swap / v_permlane32_swap applied to two copies of v), which hand every
+// lane its own value and its partner's i ^ m, in an order that depends on the lane; the
+// reductions here are symmetric in the two, so both are passed on.
+template <int M>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8, "DPP steps");
+    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+}
+template <int M>
+__device__ __forceinline__ void swap_pair(uint32_t v, uint32_t& a, uint32_t& b) {
+    static_assert(M == 16 || M == 32, "lane-swap steps");
+    if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        a = r[0], b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        a = r[0], b = r[1];
+    }
+}
+
+// One butterfly step of a sum: own value plus the partner's (fp addition is commutative,
+// so the order of the two operands does not change the result).
+template <int M>
+__device__ __forceinline__ float sum_step(float v) {
+    if constexpr (M <= 8) {
+        return v + __uint_as_float(dpp_partner<M>(__float_as_uint(v)));
+    } else {
+        uint32_t a, b;
+        swap_pair<M>(__float_as_uint(v), a, b);
+        return __uint_as_float(a) + __uint_as_float(b);
+    }
+}
+
+// Sum over lanes [0, P) by a butterfly (P a power of two, at most 64): every lane of the
+// group ends with the pairwise-tree sum ((v0+v1)+(v2+v3))+..., the same value on every
+// lane.
 __device__ __forceinline__ float butterfly_sum(float v, int P) {
-    for (int m = 1; m < P; m <<= 1) v = v + __shfl_xor(v, m, MOE_WAVE);
+    if (P > 1) v = sum_step<1>(v);
+    if (P > 2) v = sum_step<2>(v);
+    if (P > 4) v = sum_step<4>(v);
+    if (P > 8) v = sum_step<8>(v);
+    if (P > 16) v = sum_step<16>(v);
+    if (P > 32) v = sum_step<32>(v);
     return v;
 }
 
+template <int M>
+__device__ __forceinline__ float max_step(float v) {
+    if constexpr (M <= 8) {
+        return fmaxf(v, __uint_as_float(dpp_partner<M>(__float_as_uint(v))));
+    } else {
+        uint32_t a, b;
+        swap_pair<M>(__float_as_uint(v), a, b);
+        return fmaxf(__uint_as_float(a), __uint_as_float(b));
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, MOE_WAVE));
-    return v;
+    v = max_step<1>(v);
+    v = max_step<2>(v);
+    v = max_step<4>(v);
+    v = max_step<8>(v);
+    v = max_step<16>(v);
+    return max_step<32>(v);
+}
+
+// One step of the wave-wide maximum of the 64-bit key (hi, lo).
+__device__ __forceinline__ void key_max(uint32_t& h, uint32_t& l, uint32_t oh, uint32_t ol) {
+    const bool take = (oh > h) || (oh == h && ol > l);
+    h = take ? oh : h;
+    l = take ? ol : l;
+}
+template <int M>
+__device__ __forceinline__ void key_step(uint32_t& h, uint32_t& l) {
+    if constexpr (M <= 8) {
+        key_max(h, l, dpp_partner<M>(h), dpp_partner<M>(l));
+    } else {
+        uint32_t h0, h1, l0, l1;
+        swap_pair<M>(h, h0, h1);
+        swap_pair<M>(l, l0, l1);
+        h = h0, l = l0;
+        key_max(h, l, h1, l1);
+    }
 }
 
 // Softmax over E logits held one per lane (lane < E), top-K by (p desc, e asc),
@@ -82,14 +159,12 @@ __device__ void softmax_topk_token(float logit, int E, int K, int64_t t,
     float sel_p = 0.0f;
     for (int k = 0; k < K; ++k) {
         uint32_t bh = khi, bl = klo;
-#pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) {
-            uint32_t oh = __shfl_xor(bh, msk, MOE_WAVE);
-            uint32_t ol = __shfl_xor(bl, msk, MOE_WAVE);
-            bool take = (oh > bh) || (oh == bh && ol > bl);
-            bh = take ? oh : bh;
-            bl = take ? ol : bl;
-        }
+        key_step<1>(bh, bl);
+        key_step<2>(bh, bl);
+        key_step<4>(bh, bl);
+        key_step<8>(bh, bl);
+        key_step<16>(bh, bl);
+        key_step<32>(bh, bl);
         int e = (int)(0xFFFFu - bl);
         if (lane == e) { khi = 0u; klo = 0u; }
         if (lane == k) { sel_e = e; sel_p = __uint_as_float(bh); }
@@ -105,85 +180,129 @@ __device__ void softmax_topk_token(float logit, int E, int K, int64_t t,
 // ---------------------------------------------------------------------------------
 // Router GEMM, bf16 on MFMA: a block of W waves takes 16 tokens; the waves split d
 // (split-K, W = 8 when d % 256 == 0, else 4) and each computes 16 tokens x 16*NB expert
-// columns with v_mfma_f32_16x16x32_bf16, keeping RT_LOADS 16-byte loads of x per lane in
-// flight (the kernel streams x once and is bound by HBM); the W partial sums are added
-// in a fixed order in LDS. Column E (if present) is the shared expert's gate vector w_sg.
+// columns with v_mfma_f32_16x16x32_bf16; the W partial sums are added in a fixed order
+// in LDS. Column E (if present) is the shared expert's gate vector w_sg.  A wave's
+// slice of d is short (768 k for d = 6144), so the kernel is bound by load latency
+// unless many loads are in flight: a lane loads its x fragments and the matching
+// weight fragments (L2-resident, shared by every block) of BL k-steps together, and the
+// loads of the next BL k-steps are issued before the current ones are used (two
+// register buffers).  Every wave adds its k-steps in ascending order, so the sums do not
+// depend on BL.
 // ---------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int RT_TOK = 16;     // tokens per block
 constexpr int RT_NBMAX = 5;    // up to 80 columns (64 experts + shared gate)
-constexpr int RT_LOADS = 8;    // k-steps of x loaded ahead per lane
 
-// w_rt: [NB*16][d] bf16, the router weight transposed (row e = column e of w_router,
-// row E = w_sg, zero rows after).
-__global__ void __launch_bounds__(256) transpose_router_w(const bf16_t* __restrict__ w,
+// w_frag: the router weight (and w_sg as column E, zero columns up to 16 NB) in the
+// order the MFMA B fragments are read: for k-step s (32 k) and column block j, 1 KB of
+// 64 lanes x 8 bf16, lane q holding column 16 j + (q & 15), k = 32 s + 8 (q >> 4) + 0..7.
+// A wave's fragment load is then 1 KB of consecutive bytes (eight whole 128-byte lines)
+// at a wave-uniform offset.
+__global__ void __launch_bounds__(256) router_w_fragments(const bf16_t* __restrict__ w,
                                                           const bf16_t* __restrict__ w_sg,
-                                                          bf16_t* __restrict__ w_rt, int d,
-                                                          int E, int ncol) {
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= (int64_t)ncol * d) return;
-    int e = (int)(i / d);
-    int k = (int)(i % d);
+                                                          bf16_t* __restrict__ w_frag, int d,
+                                                          int E, int NB) {
+    const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (o >= (int64_t)NB * 16 * d) return;
+    const int e8 = (int)(o & 7);
+    const int q = (int)((o >> 3) & 63);
+    const int64_t blk = o >> 9;
+    const int j = (int)(blk % NB);
+    const int64_t ks = blk / NB;
+    const int col = 16 * j + (q & 15);
+    const int64_t k = ks * 32 + 8 * (q >> 4) + e8;
     bf16_t v = 0;
-    if (e < E) v = w[(int64_t)k * E + e];
-    else if (e == E && w_sg) v = w_sg[k];
-    w_rt[i] = v;
+    if (col < E) v = w[k * E + col];
+    else if (col == E && w_sg) v = w_sg[k];
+    w_frag[o] = v;
 }
 
-template <int W>
+template <int W, int NB>
 __global__ void __launch_bounds__(64 * W) router_fwd_mfma(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_rt, const float* __restrict__ bias,
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_frag, const float* __restrict__ bias,
     float* __restrict__ logits, float* __restrict__ sg_logit, int T, int d, int E, int K,
-    int NB, int has_sg, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
+    int has_sg, int32_t* __restrict__ topk_idx, float* __restrict__ topk_prob,
     float* __restrict__ topk_gate) {
+    static_assert(NB >= 1 && NB <= RT_NBMAX, "1 to 5 column blocks");
+    // k-steps per register buffer: (1 + NB) 16-byte loads per k-step and lane, two buffers
+    constexpr int BL = NB <= 2 ? 8 : 4;
     __shared__ float part[W][RT_TOK][RT_NBMAX * 16 + 1];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int t0 = blockIdx.x * RT_TOK;
     const int row = lane & 15;      // token within the block (A) / column (B)
     const int kq = lane >> 4;       // which 8-wide k group of the 32
-    const int dslice = d / W;
+    const int dslice = d / W;       // a multiple of 32
     const int kbeg = wave * dslice;
 
-    f32x4_t acc[RT_NBMAX];
+    f32x4_t acc[NB];
 #pragma unroll
-    for (int j = 0; j < RT_NBMAX; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int tok = t0 + row;
     const bool tok_ok = tok < T;
-    // rows past T read token 0 (a valid row) and are zeroed
-    const bf16_t* xa = x + (int64_t)(tok_ok ? tok : 0) * d + kbeg + kq * 8;
-    const bf16_t* wb0 = w_rt + (int64_t)row * d + kbeg + kq * 8;
-    auto step = [&](const u32x4& av, int k) {
-        const u32x4 az = tok_ok ? av : u32x4{0, 0, 0, 0};
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, az);
+    // Buffer loads: a per-lane byte offset and a wave-uniform one (the k-step, and for the
+    // weight the column block) against a resource over the block's rows of x, or over the
+    // transposed weight.  Rows past T read the block's first row and are zeroed.  A k-step
+    // at or past the slice's end (loaded with its batch, never used) loads the slice's
+    // last k-step again, so every access stays inside the wave's own slice.
+    const int rows = min(RT_TOK, T - t0);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (int64_t)t0 * d), 0, rows * d * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)w_frag, 0, NB * 16 * d * 2, 0x00020000);
+    const int xo = ((tok_ok ? row : 0) * d + kbeg + kq * 8) * 2;
+    const int wo = lane * 16;
+    const int ks0 = kbeg / 32;  // the wave's first k-step
+
+    // Loads of the BL k-steps from k.
+    auto load = [&](u32x4 (&xv)[BL], u32x4 (&wv)[BL][NB], int k) {
 #pragma unroll
-        for (int j = 0; j < RT_NBMAX; ++j) {
-            if (j < NB) {
-                const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *(const u32x4*)(wb0 + (int64_t)j * 16 * d + k));
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+        for (int u = 0; u < BL; ++u) {
+            const int ku = min(k + 32 * u, dslice - 32);
+            xv[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, ku * 2, 0));
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                wv[u][j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo, ((ks0 + ku / 32) * NB + j) * 1024, 0));
+        }
+    };
+    auto compute = [&](const u32x4 (&xv)[BL], const u32x4 (&wv)[BL][NB], int k) {
+#pragma unroll
+        for (int u = 0; u < BL; ++u) {
+            if (k + 32 * u < dslice) {
+                const u32x4 az = tok_ok ? xv[u] : u32x4{0, 0, 0, 0};
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, az);
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, __builtin_bit_cast(bf16x8_t, wv[u][j]), acc[j], 0, 0, 0);
             }
         }
     };
-    int k = 0;
-    for (; k + 32 * RT_LOADS <= dslice; k += 32 * RT_LOADS) {
-        u32x4 av[RT_LOADS];
-#pragma unroll
-        for (int u = 0; u < RT_LOADS; ++u) av[u] = *(const u32x4*)(xa + k + 32 * u);
-#pragma unroll
-        for (int u = 0; u < RT_LOADS; ++u) step(av[u], k + 32 * u);
+    // Two register buffers; the last batch is computed on its own branch, so that each
+    // compute follows its loads' issue in straight-line code (the compiler then waits for
+    // those loads only, not for the next batch's).
+    u32x4 x0[BL], x1[BL], w0[BL][NB], w1[BL][NB];
+    constexpr int KB = 32 * BL;
+    load(x0, w0, 0);
+    for (int k = 0;;) {
+        if (k + KB >= dslice) { compute(x0, w0, k); break; }
+        load(x1, w1, k + KB);
+        compute(x0, w0, k);
+        k += KB;
+        if (k + KB >= dslice) { compute(x1, w1, k); break; }
+        load(x0, w0, k + KB);
+        compute(x1, w1, k);
+        k += KB;
     }
-    for (; k < dslice; k += 32) step(*(const u32x4*)(xa + k), k);
     // D layout of the 16x16 MFMA: lane holds column (lane & 15), rows 4*(lane>>4)+i.
 #pragma unroll
-    for (int j = 0; j < RT_NBMAX; ++j) {
-        if (j < NB) {
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[wave][4 * kq + i][j * 16 + row] = acc[j][i];
-        }
-    }
+        for (int i = 0; i < 4; ++i) part[wave][4 * kq + i][j * 16 + row] = acc[j][i];
     __syncthreads();
     // Each wave finishes RT_TOK / W tokens: fixed-order sum of the W split-K partials,
     // bias, then softmax and top-K with one lane per expert.
@@ -598,17 +717,26 @@ hipError_t launch_router_fwd(const moe_desc& d, const void* x, const void* w_rou
         const int NB = (ncol + 15) / 16;
         bf16_t* wrt = (bf16_t*)w_rt_ws;
         int64_t n = (int64_t)NB * 16 * d.d;
-        transpose_router_w<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-            (const bf16_t*)w_router, (const bf16_t*)w_sg, wrt, d.d, d.E, NB * 16);
+        router_w_fragments<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
+            (const bf16_t*)w_router, (const bf16_t*)w_sg, wrt, d.d, d.E, NB);
         const unsigned nb = (d.T + RT_TOK - 1) / RT_TOK;
-        if (d.d % 256 == 0)
-            router_fwd_mfma<8><<<nb, 512, 0, s>>>(
-                (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB,
+        auto launch = [&](auto w_tag, auto nb_tag) {
+            constexpr int W = decltype(w_tag)::value, NBc = decltype(nb_tag)::value;
+            router_fwd_mfma<W, NBc><<<nb, 64 * W, 0, s>>>(
+                (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K,
                 w_sg ? 1 : 0, r.topk_idx, r.topk_prob, r.topk_gate);
-        else
-            router_fwd_mfma<4><<<nb, 256, 0, s>>>(
-                (const bf16_t*)x, wrt, bias, logits, sg_logit, d.T, d.d, d.E, d.K, NB,
-                w_sg ? 1 : 0, r.topk_idx, r.topk_prob, r.topk_gate);
+        };
+        auto by_nb = [&](auto w_tag) {
+            switch (NB) {
+                case 1: launch(w_tag, std::integral_constant<int, 1>{}); break;
+                case 2: launch(w_tag, std::integral_constant<int, 2>{}); break;
+                case 3: launch(w_tag, std::integral_constant<int, 3>{}); break;
+                case 4: launch(w_tag, std::integral_constant<int, 4>{}); break;
+                default: launch(w_tag, std::integral_constant<int, 5>{}); break;
+            }
+        };
+        if (d.d % 256 == 0) by_nb(std::integral_constant<int, 8>{});
+        else by_nb(std::integral_constant<int, 4>{});
     } else if (d.dtype == MOE_BF16) {
         router_fwd_valu<bf16_t><<<d.T, 64, 0, s>>>(
             (const bf16_t*)x, (const bf16_t*)w_router, bias, (const bf16_t*)w_sg, logits, sg_logit,

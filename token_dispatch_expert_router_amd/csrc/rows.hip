@@ -673,6 +673,194 @@ __global__ void __launch_bounds__(256) router_wgrad_partial_wide(
         }
 }
 
+// bf16 layers: partial[c][i][e] = sum over the tokens t of chunk c (RG_CHUNK tokens) of
+// x[t][i] * dcol[t][e], on the bf16 matrix cores.  dcol (fp32) is split into two bf16
+// terms, hi = bf16(v) and lo = bf16(v - hi), whose sum carries 16 significant bits (a
+// relative error below 2^-17, far under the bf16 rounding of dW); x is bf16 already, so
+// both products are exact and the MFMA accumulates them in fp32.  A block takes 128 i
+// and one chunk, in k-steps of 32 tokens staged through LDS with two buffers: x as it
+// is in memory ([32 t][128 i], 256-byte rows, 16-byte chunks XOR-swizzled, read as MFMA
+// fragments with the LDS transpose read) and hi, lo transposed ([e][32 t], one 16-byte
+// read per fragment).  Wave w owns i0 + 32 w .. +31 (two 16-row A tiles) and all CT
+// 16-column tiles.
+constexpr int RG_I = 128;
+constexpr int RG_CHUNK = 512;
+constexpr int RG_DEPTH = 4;    // register sets of the staging pipeline
+
+typedef __bf16 rg_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short rg_s16x4 __attribute__((ext_vector_type(4)));
+typedef short rg_s16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t rg_u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte chunk swizzle of a [32 t][128 i] tile: chunk p of row t holds logical chunk
+// p ^ rg_swz(t); the transpose reads of a fragment (4 rows x 32 bytes per 16 lanes) then
+// fall on distinct banks.
+__device__ __forceinline__ int rg_swz(int t) { return (4 * (t & 3)) ^ (((t >> 3) & 1) << 1); }
+
+template <int CT>
+__global__ void __launch_bounds__(256) router_wgrad_mfma(const bf16_t* __restrict__ x,
+                                                         const float* __restrict__ dl,
+                                                         const float* __restrict__ dz, int T_,
+                                                         int d, int E, int ncol,
+                                                         float* __restrict__ partial) {
+    constexpr int NC = CT * 16;       // columns, zero past ncol
+    constexpr int PT = 40;            // row pitch (bf16) of the transposed hi, lo tiles
+    constexpr int NPAIR = NC * 4;     // (column, 8-token group) pairs per k-step
+    constexpr int PPT = (NPAIR + 255) / 256;
+    __shared__ __attribute__((aligned(16))) char sx[2][32 * 256];
+    __shared__ __attribute__((aligned(16))) bf16_t sh[2][NC][PT];
+    __shared__ __attribute__((aligned(16))) bf16_t sl[2][NC][PT];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int i0 = blockIdx.x * RG_I;
+    const int64_t tb = (int64_t)blockIdx.y * RG_CHUNK;
+    const int nt = (int)min((int64_t)RG_CHUNK, (int64_t)T_ - tb);
+    const int nks = (nt + 31) / 32;
+
+    // staging: x rows t = tid / 16 and t + 16, chunk tid % 16 (8 i); dcol pairs
+    // p = tid + 256 j: column p / 4, tokens 8 (p % 4) .. +7.  The loads of a k-step go into
+    // one of RG_DEPTH register sets, RG_DEPTH - 1 k-steps ahead of its LDS stores.
+    const int xt = tid >> 4, xch = tid & 15;
+    const bool x_ok = i0 + 8 * xch < d;  // d % 8 == 0: a chunk is wholly in or out
+    const bf16_t* xs = x + tb * d + (x_ok ? i0 + 8 * xch : 0);
+    // column source of each pair: dl (stride E), dz (stride 1), or none (reads dl, zeroed)
+    const float* csrc[PPT];
+    int cstride[PPT];
+    bool clive[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int p = tid + 256 * j;
+        const int e = p >> 2;
+        const bool in = p < NPAIR;
+        const bool from_dz = in && e == E && dz;
+        clive[j] = in && (e < E || from_dz);
+        csrc[j] = from_dz ? dz + tb : dl + tb * E + (in && e < E ? e : 0);
+        cstride[j] = from_dz ? 1 : E;
+    }
+    // Every load is issued unconditionally from a valid address (tokens past the chunk read
+    // its last token); values that do not exist are zeroed when they are stored to LDS.
+    struct Regs {
+        u32x4 x[2];
+        float c[PPT][8];
+    };
+    auto load_regs = [&](Regs& R, int ks) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tl = min(32 * ks + xt + 16 * h, nt - 1);
+            R.x[h] = *(const u32x4*)(xs + (int64_t)tl * d);
+        }
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int tg = (tid + 256 * j) & 3;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int tl = min(32 * ks + 8 * tg + u, nt - 1);
+                R.c[j][u] = csrc[j][(int64_t)tl * cstride[j]];
+            }
+        }
+    };
+    auto store_lds = [&](const Regs& R, int ks, int b) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = xt + 16 * h;
+            const bool ok = x_ok && 32 * ks + t < nt;
+            *(u32x4*)(sx[b] + t * 256 + ((xch ^ rg_swz(t)) << 4)) = ok ? R.x[h] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int p = tid + 256 * j;
+            if (p < NPAIR) {
+                const int e = p >> 2, tg = p & 3;
+                float hi[8], lo[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float v = (clive[j] && 32 * ks + 8 * tg + u < nt) ? R.c[j][u] : 0.f;
+                    hi[u] = bf16_to_f32(f32_to_bf16(v));
+                    lo[u] = v - hi[u];
+                }
+                *(u32x4*)&sh[b][e][8 * tg] = Vec16<bf16_t>::pack(hi);
+                *(u32x4*)&sl[b][e][8 * tg] = Vec16<bf16_t>::pack(lo);
+            }
+        }
+    };
+
+    f32x4_t acc[2][CT];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[a][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // fragment addresses: A (x^T, rows i) by the transpose read of 4 rows x 8 bytes per
+    // 16 lanes (lane s of group g: k row 8 g + s / 4, columns 4 (s % 4) .. +3; the second
+    // read 4 k rows further); B (hi, lo) one 16-byte read of 8 tokens of column lane % 16
+    const int g = lane >> 4, sl16 = lane & 15;
+    uint32_t a_off[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int col = 32 * wave + 16 * a + 4 * (sl16 & 3);
+        const int kr = 8 * g + (sl16 >> 2);
+        a_off[a] = kr * 256 + (((col >> 3) ^ rg_swz(kr)) << 4) + (col & 7) * 2;
+    }
+    auto compute = [&](int b) {
+        typedef __attribute__((address_space(3))) rg_s16x4 lds_s16x4;
+        rg_bf16x8 af[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(sx[b]) + a_off[a];
+            const rg_s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)base);
+            const rg_s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + 1024));
+            const rg_s16x8 v = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            af[a] = __builtin_bit_cast(rg_bf16x8, v);
+        }
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            const rg_bf16x8 bh = __builtin_bit_cast(rg_bf16x8, *(const rg_u32x4*)&sh[b][16 * c + sl16][8 * g]);
+            const rg_bf16x8 bl = __builtin_bit_cast(rg_bf16x8, *(const rg_u32x4*)&sl[b][16 * c + sl16][8 * g]);
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bh, acc[a][c], 0, 0, 0);
+                acc[a][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bl, acc[a][c], 0, 0, 0);
+            }
+        }
+    };
+
+    // Loads run RG_DEPTH - 1 k-steps ahead; near the chunk's end they repeat its last
+    // k-step (unused), so that they are issued unconditionally.  LDS buffer ks & 1 is
+    // written after the barrier that ends the compute of k-step ks - 2.
+    Regs R[RG_DEPTH];
+    if (nks > 0) {
+#pragma unroll
+        for (int j = 0; j < RG_DEPTH - 1; ++j) load_regs(R[j], min(j, nks - 1));
+    }
+    for (int ks0 = 0; ks0 < nks; ks0 += RG_DEPTH) {
+#pragma unroll
+        for (int u = 0; u < RG_DEPTH; ++u) {
+            const int ks = ks0 + u;
+            if (ks >= nks) break;
+            load_regs(R[(u + RG_DEPTH - 1) % RG_DEPTH], min(ks + RG_DEPTH - 1, nks - 1));
+            store_lds(R[u], ks, ks & 1);
+            __syncthreads();
+            compute(ks & 1);
+        }
+    }
+    // D of the 16x16 MFMA: lane holds column e = 16 c + lane % 16 and rows
+    // i = 4 (lane / 16) + r of the A tile
+    const int ncol8 = (ncol + 7) / 8 * 8;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 32 * wave + 16 * a + 4 * g + r;
+            if (i >= d) continue;
+            float* out = partial + ((int64_t)blockIdx.y * d + i) * ncol8;
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const int e = 16 * c + sl16;
+                if (e < ncol) out[e] = acc[a][c][r];
+            }
+        }
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) router_wgrad_final(const float* __restrict__ partial,
                                                           int n_chunks, int d, int E, int ncol,
@@ -797,6 +985,8 @@ hipError_t launch_permute_bwd(const moe_desc& d, const void* dxp, const moe_rout
     return hipGetLastError();
 }
 
+int router_bwd_chunk(int dtype) { return dtype == MOE_BF16 ? RG_CHUNK : RW_TOK; }
+
 hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing& r,
                              const float* dgate, const float* dz, float* dlogits, void* dw_router,
                              void* dw_sg, float* partial, int n_chunks, int chunk, hipStream_t s) {
@@ -826,11 +1016,19 @@ hipError_t launch_router_bwd(const moe_desc& d, const void* x, const moe_routing
             router_wgrad_partial_wide<T, 5><<<gw, 256, 0, s>>>(xt, dlogits, dz, d.T, d.d, d.E, ncol, chunk, partial);
     };
     if (d.dtype == MOE_BF16) {
-        if (wide)
-            launch_wide(bf16_t{});
-        else if (n_chunks > 0)
-            router_wgrad_partial<bf16_t><<<g1, 256, 0, s>>>((const bf16_t*)x, dlogits, dz, d.T, d.d,
-                                                            d.E, ncol, chunk, partial);
+        // chunks of RG_CHUNK tokens on the bf16 matrix cores
+        if (chunk != RG_CHUNK || ct > RW_CT) return hipErrorInvalidValue;
+        const dim3 gm(blocks_for(d.d, RG_I), n_chunks);
+        const bf16_t* xb = (const bf16_t*)x;
+        if (n_chunks > 0) {
+            switch (ct) {
+                case 1: router_wgrad_mfma<1><<<gm, 256, 0, s>>>(xb, dlogits, dz, d.T, d.d, d.E, ncol, partial); break;
+                case 2: router_wgrad_mfma<2><<<gm, 256, 0, s>>>(xb, dlogits, dz, d.T, d.d, d.E, ncol, partial); break;
+                case 3: router_wgrad_mfma<3><<<gm, 256, 0, s>>>(xb, dlogits, dz, d.T, d.d, d.E, ncol, partial); break;
+                case 4: router_wgrad_mfma<4><<<gm, 256, 0, s>>>(xb, dlogits, dz, d.T, d.d, d.E, ncol, partial); break;
+                default: router_wgrad_mfma<5><<<gm, 256, 0, s>>>(xb, dlogits, dz, d.T, d.d, d.E, ncol, partial); break;
+            }
+        }
         router_wgrad_final<bf16_t><<<g2, 256, 0, s>>>(partial, n_chunks, d.d, d.E, ncol,
                                                        (bf16_t*)dw_router, (bf16_t*)dw_sg);
     } else {
