@@ -96,6 +96,23 @@ static int check_wgrad(int mode, const char* name, int E, int64_t R, int d, int 
         }
         if (mx - mn > 1) return fail(name, "uneven XCD share of an expert", e, mn, mx);
     }
+    // The persistent launch: P blocks (a multiple of 8, at most G), block p walking
+    // b = p, p + P, ... and stopping at the first b without a tile; every tile must again
+    // be produced exactly once, by a block on the XCD b % 8 of its one-tile-per-block launch.
+    for (int P : {256, 64, 8}) {
+        const int64_t PP = P < G ? P : G;
+        std::vector<int> seen_p((size_t)E * MT * NT, 0);
+        for (int64_t p = 0; p < PP; ++p)
+            for (int64_t b = p;; b += PP) {
+                int e, mi, ni;
+                if (b > 0x7FFFFFFF || !tiles::wgrad_tile((int)b, E, MT, NT, e, mi, ni)) break;
+                if (b % 8 != p % 8) return fail(name, "persistent walk changed XCD", (long)p, (long)b, 0);
+                if (++seen_p[((size_t)e * MT + mi) * NT + ni] != 1)
+                    return fail(name, "persistent walk: tile produced twice", e, mi, ni);
+            }
+        for (size_t i = 0; i < seen_p.size(); ++i)
+            if (seen_p[i] != 1) return fail(name, "persistent walk: tile never produced", (long)i, P, 0);
+    }
     printf("%s blocks %lld tiles %d ok\n", name, (long long)G, E * MT * NT);
     return 0;
 }

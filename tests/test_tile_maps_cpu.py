@@ -5,7 +5,9 @@ decode of segmented rows, the grouped m/n order and the weight-gradient split) a
 compiled for the CPU into tests/native/tile_map_check, which walks every block of each of
 the six launches and asserts that every output tile is produced exactly once, inside its
 segment, with each XCD on one contiguous range of tiles (row passes) or an equal share of
-every expert (weight gradients).  Offsets: each bf16 layer shape routed by the oracle
+every expert (weight gradients); for the weight gradients it also walks the persistent
+launch (256, 64 or 8 blocks, each stepping through the one-tile launch's blocks of its
+XCD until the first without a tile) and asserts the same exact-once coverage.  Offsets: each bf16 layer shape routed by the oracle
 on router inputs drawn on the CPU (the same recipe and sizes as on the GPU; the CPU
 generator's values differ from the GPU's, so the segments are of the same distribution,
 not identical; the GPU test runs the same check on the device's own offsets), plus

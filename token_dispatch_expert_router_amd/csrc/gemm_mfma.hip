@@ -53,7 +53,11 @@
 // that each XCD runs a contiguous range, in which consecutive tiles form 4 x 8 blocks
 // (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2.  The
 // weight-gradient passes, whose tiles' K is their expert's segment length, give each
-// XCD an equal contiguous share of every expert instead.
+// XCD an equal contiguous share of every expert instead; with short segments they run
+// as one persistent block per CU that carries the operand ring from tile to tile
+// (gg_wgrad_kernel).
+#include <algorithm>
+
 #include "common.h"
 #include "tile_map.h"
 
@@ -784,6 +788,298 @@ gg_mfma_kernel(GemmArgs g) {
     gg_tile<MODE, PAIRED, 8>(g, smem_base, e, m0, m_lim, n0, k_lo, k_hi, nk);
 }
 
+// Weight gradients with short segments, persistent.  One block per CU walks the tiles that
+// tiles::wgrad_tile gives its XCD, in the same order as a one-tile-per-block launch, and
+// keeps the operand ring running across tile boundaries: during the last three compute
+// phases of a tile (when it has at least three k-steps) the refills fetch the next
+// tile's first three k-steps, so that tile starts on data already in LDS, and the
+// epilogue's stores (128 KB per tile) drain while it runs instead of ahead of its first
+// loads.  The stage index runs on over tiles (k-step j of a tile whose first k-step is
+// the block's g0-th sits in stage (g0 + j) % 4); the epilogue stages its results in the
+// one stage no load targets at that moment, 32 rows per wave at a time.
+//
+// Waits.  vmcnt counts loads and stores together and retires them in order.  When a
+// tile's first k-steps were issued by the previous tile, the previous epilogue's 16
+// stores per wave sit between them and the tile's own later loads, so the waits for
+// those k-steps (k-steps 0..2) allow the stores to stay in flight; every other wait
+// counts exactly the loads issued after the one it waits for.
+constexpr int WG_STORES = 16;  // global stores per wave in a weight-gradient epilogue
+
+__device__ __forceinline__ void wait_vm(int n) {
+    // n: loads and stores allowed to stay in flight (a multiple of 4, at most 28)
+    switch (n) {
+        case 28: asm volatile("s_waitcnt vmcnt(28)" ::: "memory"); break;
+        case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+        case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+        case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+struct WgTile {
+    int e, m0, n0, k_lo, nrows, nk;
+    bool ok;
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+gg_wgrad_kernel(GemmArgs g) {
+    static_assert(MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP, "weight gradients");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * SLOT_BYTES];
+    const uint32_t smem_base = (uint32_t)(uintptr_t)(lds_void*)smem;
+    const int d = g.d, f = g.f;
+    int MT, NTl;
+    tiles::wgrad_dims(MODE, d, f, MT, NTl);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wv >> 2;   // group 0 loads A (rows m of dW), group 1 loads B (columns n)
+    const int wq = wv & 3;
+    const int wm = wv & 1;
+    const int wn = wv >> 1;
+    const bf16_t* A0 = (const bf16_t*)g.A0;
+    const bf16_t* B0 = (const bf16_t*)g.B0;
+    const bf16_t* B1 = (const bf16_t*)g.B1;
+    // row pitch of this wave's operand: A = h ([rows][f]) or xp ([rows][d]); B = d_o
+    // ([rows][d]) or da, db ([rows][f])
+    const int64_t ld = grp == 0 ? (MODE == GG_WGRAD_DOWN ? f : d) : (MODE == GG_WGRAD_DOWN ? d : f);
+    const uint64_t kstride = (uint64_t)BK * ld * 2;
+    // per-lane byte offsets of this wave's four direct loads (MN-major: instruction ii
+    // covers k rows 2 ii + lane / 32, physical chunk lane % 32), without the tile's column
+    uint32_t vbase[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int ii = wq * 4 + u;
+        const int kr = ii * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ swz_mn(kr);
+        vbase[u] = (uint32_t)(((int64_t)kr * ld + c * 8) * 2);
+    }
+    uint32_t a_rd[8], b_rd[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a_rd[i] = addr_mn(0, wm * 128 + i * 16, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b_rd[j] = addr_mn(STEP_TILE_BYTES, wn * 64 + j * 16, lane);
+
+    // The segment offsets are read with scalar loads (through the constant address
+    // space): a vector load here would be followed by a wait for every vector memory
+    // operation in flight, the previous epilogue's stores and the prefetched k-steps
+    // included.
+    typedef const __attribute__((address_space(4))) int32_t const_i32;
+    const_i32* offs = (const_i32*)g.offsets;
+    auto decode = [&](int64_t b) {
+        WgTile t{0, 0, 0, 0, 0, 0, false};
+        int e, mi, ni;
+        if (b > 0x7FFFFFFF || !tiles::wgrad_tile((int)b, g.E, MT, NTl, e, mi, ni)) return t;
+        e = __builtin_amdgcn_readfirstlane(e);
+        t.ok = true;
+        t.e = e;
+        t.m0 = __builtin_amdgcn_readfirstlane(mi) * BM;
+        t.n0 = __builtin_amdgcn_readfirstlane(ni) * BN;
+        t.k_lo = offs[e];
+        t.nrows = offs[e + 1] - t.k_lo;
+        t.nk = (t.nrows + BK - 1) / BK;
+        return t;
+    };
+    // this wave's operand of tile t: base at the segment's first row, and the column
+    auto src_base = [&](const WgTile& t) -> uint64_t {
+        if (grp == 0) return (uint64_t)(A0 + (int64_t)t.k_lo * ld);
+        if (MODE == GG_WGRAD_DOWN) return (uint64_t)(B0 + (int64_t)t.k_lo * d);
+        return (uint64_t)((t.n0 < f ? B0 : B1) + (int64_t)t.k_lo * f);
+    };
+    auto src_col = [&](const WgTile& t) -> int {
+        return grp == 0 ? t.m0 : (MODE == GG_WGRAD_GATEUP && t.n0 >= f ? t.n0 - f : t.n0);
+    };
+    // load u of k-step kt of a tile into stage st; k rows past the segment read as zeros
+    auto issue_one = [&](const WgTile& t, uint64_t base, int col, int kt, int st, int u) {
+        const uint32_t dst = smem_base + st * STEP_STAGE_BYTES + grp * STEP_TILE_BYTES + (wq * 4 + u) * 1024;
+        const int64_t nb = ((int64_t)t.nrows - (int64_t)kt * BK) * ld * 2;
+        const uint32_t bytes = nb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)nb;
+        lds_dma16_buf(make_rsrc(base + (uint64_t)kt * kstride, bytes), vbase[u] + (uint32_t)col * 2, dst);
+    };
+
+    Frag<8> fa;
+    Frag<4> fb;
+    auto read_stage = [&](uint32_t stage) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ds_tr_pair(fa.lo[i], fa.hi[i], stage + a_rd[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ds_tr_pair(fb.lo[j], fb.hi[j], stage + b_rd[j]);
+    };
+
+    int64_t b = blockIdx.x;
+    WgTile cur = decode(b);
+    int g0 = 0;   // the block's k-steps before this tile (stage of k-step j: (g0 + j) & 3)
+    int pre = 0;  // this tile's k-steps issued by the previous tile (0, or min(3, nk))
+    while (cur.ok) {
+        const WgTile nxt = decode(b + gridDim.x);
+        const int nk = cur.nk;
+        const bool pf = nk >= 3 && nxt.ok && nxt.nk > 0;
+        const uint64_t cbase = src_base(cur);
+        const int ccol = src_col(cur);
+        const uint64_t nbase = pf ? src_base(nxt) : 0;
+        const int ncol = pf ? src_col(nxt) : 0;
+        // targets j >= 0 of this tile's load sequence: own k-step j, or the next tile's
+        // k-step j - nk (issued during compute phase j - 3)
+        auto issued = [&](int j) -> int { return (j < nk || (pf && j - nk < nxt.nk)) ? 1 : 0; };
+        auto issue_target = [&](int j, int u) {
+            const int st = (g0 + j) & (STEP_STAGES - 1);
+            if (j < nk) issue_one(cur, cbase, ccol, j, st, u);
+            else issue_one(nxt, nbase, ncol, j - nk, st, u);
+        };
+        // stores of the previous epilogue still allowed in flight when waiting for k-step j
+        auto held = [&](int j) -> int { return (pre > 0 && j <= 2) ? WG_STORES : 0; };
+
+        f32x4_t acc[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+
+        if (nk > 0) {
+            const int n3 = min(nk, 3);
+            if (pre == 0) {
+                for (int j = 0; j < n3; ++j) {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) issue_target(j, u);
+                }
+            }
+            wait_vm(4 * (n3 - 1) + held(0));
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            if (grp == 1) __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+
+            // the compute phase of k-step kt loads target kt + 3: its source, column and the
+            // bytes left in its segment are carried from phase to phase
+            const int64_t kbytes = (int64_t)BK * ld * 2;
+            bool tvalid;
+            uint64_t tbase;
+            int64_t tnb;
+            uint32_t tcol2;
+            if (3 < nk) {
+                tvalid = true;
+                tbase = cbase + 3 * kstride;
+                tnb = ((int64_t)cur.nrows - 3 * BK) * ld * 2;
+                tcol2 = (uint32_t)ccol * 2;
+            } else {
+                tvalid = pf && 3 - nk < nxt.nk;
+                tbase = nbase + (uint64_t)(3 - nk) * kstride;
+                tnb = ((int64_t)nxt.nrows - (int64_t)(3 - nk) * BK) * ld * 2;
+                tcol2 = (uint32_t)ncol * 2;
+            }
+            for (int kt = 0; kt < nk; ++kt) {
+                // ---- memory phase
+                read_stage(smem_base + ((g0 + kt) & (STEP_STAGES - 1)) * STEP_STAGE_BYTES);
+                const bool refill = tvalid;
+                const uint64_t rbase = tbase;
+                const uint32_t rbytes = tnb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)tnb;
+                const uint32_t rcol2 = tcol2;
+                const uint32_t rdst = smem_base + ((g0 + kt + 3) & (STEP_STAGES - 1)) * STEP_STAGE_BYTES +
+                                      grp * STEP_TILE_BYTES + wq * 4 * 1024;
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (grp == 1 && kt + 1 < nk) {
+                    if (kt >= 2 && kt + 2 < nk) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                    else wait_vm(4 * issued(kt + 2) + held(kt + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                // ---- compute phase, with this wave's four loads of target kt + 3
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    const int i = q >> 2, j = (i & 1) ? 3 - (q & 3) : (q & 3);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        frag_value<true>(fb, j), frag_value<true>(fa, i), acc[i][j], 0, 0, 0);
+                    if ((q & 7) == 2 && refill) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        lds_dma16_buf(make_rsrc(rbase, rbytes), vbase[q >> 3] + rcol2, rdst + (q >> 3) * 1024);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_s_setprio(0);
+                // the next target, kt + 4: this tile's k-step, or the next tile's
+                if (kt + 4 < nk) {
+                    tbase += kstride;
+                    tnb -= kbytes;
+                } else if (kt + 4 == nk) {
+                    tvalid = pf;
+                    tbase = nbase;
+                    tnb = (int64_t)nxt.nrows * ld * 2;
+                    tcol2 = (uint32_t)ncol * 2;
+                } else {
+                    tvalid = tvalid && kt + 4 - nk < nxt.nk;
+                    tbase += kstride;
+                    tnb -= kbytes;
+                }
+                if (grp == 0 && kt + 1 < nk) {
+                    if (kt >= 2 && kt + 3 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                    else wait_vm(4 * (issued(kt + 2) + issued(kt + 3)) + held(kt + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (grp == 0) __builtin_amdgcn_s_barrier();
+        }
+
+        // ---- epilogue: bf16(acc), staged 32 rows at a time in the stage no load targets
+        // (the one after the next tile's prefetched k-steps; 4 KB per wave, rows of 128
+        // bytes whose 16-byte chunks are XOR-swizzled by row), then 16-byte streaming stores.
+        {
+            typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+            typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+            typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+            const uint32_t bbase = smem_base + ((g0 + nk + 3) & (STEP_STAGES - 1)) * STEP_STAGE_BYTES +
+                                   wv * (32 * 128);
+            const int cl = lane & 15;
+            const int cq = 4 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x4_t& a4 = acc[2 * i + h][j];
+                        const u32x2_t v = {pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3])};
+                        const int row = 16 * h + cl, col = 16 * j + cq;  // col: 4 bf16, half a chunk
+                        *(lds_u32x2*)(uintptr_t)(bbase + row * 128 + (((col >> 3) ^ (row & 7)) << 4) + (col & 7) * 2) = v;
+                    }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int q = lane + 64 * t;
+                    const int rl = q >> 3, cc = q & 7;
+                    const u32x4_t w = *(const lds_u32x4*)(uintptr_t)(bbase + rl * 128 + ((cc ^ (rl & 7)) << 4));
+                    const u32x4 v = {w[0], w[1], w[2], w[3]};
+                    const int rt = wm * 128 + i * 32 + rl;  // row within the tile
+                    const int ct = wn * 64 + cc * 8;        // column within the tile
+                    if (MODE == GG_WGRAD_DOWN) {
+                        const int64_t o = (int64_t)cur.e * f * d + (int64_t)(cur.m0 + rt) * d + cur.n0 + ct;
+                        store_stream((bf16_t*)g.C0 + o, v);
+                    } else {
+                        const bool first = cur.n0 < f;
+                        bf16_t* out = (bf16_t*)(first ? g.C0 : g.C1);
+                        const int64_t o = (int64_t)cur.e * d * f + (int64_t)(cur.m0 + rt) * f +
+                                          (first ? cur.n0 : cur.n0 - f) + ct;
+                        store_stream(out + o, v);
+                    }
+                }
+            }
+        }
+        pre = pf ? min(3, nxt.nk) : 0;
+        g0 += nk;
+        cur = nxt;
+        b += gridDim.x;
+    }
+}
+
 template <int MODE, bool PAIRED = false, bool HALF = false>
 hipError_t launch_mode(const GemmArgs& a, unsigned g8, hipStream_t s) {
     gg_mfma_kernel<MODE, PAIRED, HALF><<<g8, NTHREADS, 0, s>>>(a);
@@ -803,7 +1099,8 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
     const unsigned G = (unsigned)g8;
     // Short segments (at most 640 rows per expert by the buffer bound) leave many experts
     // a last row tile of at most 128 rows: the row passes then take the kernel that runs
-    // such a tile at half height.  Longer segments keep the kernel without that branch.
+    // such a tile at half height, and the weight gradients (whose tiles then have few
+    // k-steps) the persistent kernel.  Longer segments keep the one-tile-per-block kernels.
     const bool half = (int64_t)a.R <= 640LL * a.E;
     switch (mode) {
         case GG_FWD_GATEUP:
@@ -819,8 +1116,23 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
             if (((int64_t)a.f * 2) % 32768 == 0) return launch_mode<GG_DGRAD_GATEUP, true>(a, G, s);
             return half ? launch_mode<GG_DGRAD_GATEUP, false, true>(a, G, s)
                         : launch_mode<GG_DGRAD_GATEUP, false>(a, G, s);
-        case GG_WGRAD_DOWN: return launch_mode<GG_WGRAD_DOWN>(a, G, s);
-        default: return launch_mode<GG_WGRAD_GATEUP>(a, G, s);
+        case GG_WGRAD_DOWN:
+        default: {
+            if (!half) {
+                return mode == GG_WGRAD_DOWN ? launch_mode<GG_WGRAD_DOWN>(a, G, s)
+                                             : launch_mode<GG_WGRAD_GATEUP>(a, G, s);
+            }
+            // short segments (few k-steps per tile): one persistent block per CU (at most
+            // one fits: 128 KB of LDS), walking the same tiles as the G one-tile blocks
+            int dev = 0, cus = 0;
+            hipError_t err = hipGetDevice(&dev);
+            if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (err != hipSuccess) return err;
+            const unsigned P = (unsigned)std::min<int64_t>(G, std::max(8, cus / 8 * 8));
+            if (mode == GG_WGRAD_DOWN) gg_wgrad_kernel<GG_WGRAD_DOWN><<<P, NTHREADS, 0, s>>>(a);
+            else gg_wgrad_kernel<GG_WGRAD_GATEUP><<<P, NTHREADS, 0, s>>>(a);
+            return hipGetLastError();
+        }
     }
 }
 
