@@ -552,7 +552,10 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on the whole workload")
-        rec["cpu_baseline"] = cpu_baseline(shape, inp, lay, cap)
+        cb = cpu_baseline(shape, inp, lay, cap)
+        # the same algorithmic FLOPs as the GPU's `tflops` (grouped GEMMs + router)
+        cb["gflops"] = round((gemm_flops + router_flops) / cb["seconds"] / 1e9, 2)
+        rec["cpu_baseline"] = cb
     print(json.dumps(rec), flush=True)
 
 
