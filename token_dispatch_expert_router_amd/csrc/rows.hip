@@ -107,6 +107,12 @@ __global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ 
         constexpr bool FULL = decltype(full)::value;
         u32x4 v[C];
         load_batch<FULL>(src, c0, lane, vpr, v);
+        // Keep the batch's loads here, once: every store of them sits under a per-slot
+        // branch, into which the compiler would otherwise sink (and so repeat) the loads,
+        // behind the wait for the routing entries.  The empty asm takes the values as
+        // inputs, so the loads are issued before it and the routing load overlaps them.
+#pragma unroll
+        for (int u = 0; u < C; ++u) asm volatile("" ::"v"(v[u].x), "v"(v[u].y), "v"(v[u].z), "v"(v[u].w));
 #pragma unroll
         for (int k = 0; k < KM; ++k) {
             if (k >= K) break;
