@@ -96,6 +96,10 @@ CASES = {
     # k-steps per wave: a partial batch) and a last block of 8 tokens
     "e40_t200": _shape("e40_t200", T=200, d=640, E=40, K=4, f=256, sub_seq=200, seed=35,
                        w_std=0.05),
+    # every expert chosen by every token (K = E): the gates are the whole softmax
+    "k_eq_e": _shape("k_eq_e", T=256, d=256, E=4, K=4, f=256, seed=36, w_std=0.05),
+    # a single 16-token router block and sub-sequence
+    "t16": _shape("t16", T=16, d=256, E=8, K=2, f=256, sub_seq=16, cf=1.0, seed=37, w_std=0.05),
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
     # tile order per segment
     "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),
