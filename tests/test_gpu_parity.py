@@ -251,15 +251,23 @@ def test_route_golden_on_gpu(name):
     assert np.max(np.abs(host(lay.rt["topk_gate"]) - np.asarray(gd["topk_gate"]))) <= gd["gate_tol"]
 
 
-def _random_shapes(n=12, seed=2024):
-    """Seeded random small layers: bf16 with d, f multiples of 256 (matrix-core GEMMs)
-    or of 8 (vector-ALU GEMMs), E up to 64 with K up to 8, dropless or cf in (0.25, 2],
-    one to four sub-sequences, an optional shared expert."""
+def _random_shapes(n=24, seed=2024):
+    """Seeded random small layers: bf16 with d, f multiples of 256 (matrix-core GEMMs; d of
+    384 or 640 takes the matrix-core router with four waves per block and the vector-ALU
+    GEMMs) or of 8 (vector-ALU router and GEMMs), and some fp32 layers; E up to 64 with K up
+    to 8, dropless or cf in (0.25, 2], one to four sub-sequences, an optional shared
+    expert."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
-        mfma = bool(rng.integers(0, 2))
-        d = int(rng.choice([256, 512])) if mfma else int(8 * rng.integers(4, 40))
+        kind = int(rng.integers(0, 5))  # 0-1 matrix cores, 2 four-wave router, 3 VALU, 4 fp32
+        mfma = kind <= 1
+        if mfma:
+            d = int(rng.choice([256, 512]))
+        elif kind == 2:
+            d = int(rng.choice([384, 640]))
+        else:
+            d = int(8 * rng.integers(4, 40))
         f = int(rng.choice([256, 512, 768])) if mfma else int(8 * rng.integers(4, 40))
         E = int(rng.choice([1, 2, 3, 5, 8, 16, 32, 64]))
         K = int(rng.integers(1, min(E, 8) + 1))
@@ -267,15 +275,16 @@ def _random_shapes(n=12, seed=2024):
         S = int(rng.integers(16, 160))
         cf = None if rng.random() < 0.3 else float(np.round(rng.uniform(0.25, 2.0), 2))
         fs = int(rng.choice([0, 0, 256])) if mfma else 0
+        dtype = "f32" if kind == 4 else "bf16"
         out.append(_shape(f"rand{i}", T=n_sub * S, d=d, E=E, K=K, f=f, sub_seq=S, cf=cf, fs=fs,
-                          seed=100 + i, w_std=0.05, wr_std=0.5))
+                          seed=100 + i, w_std=0.05, wr_std=0.5, dtype=dtype))
     return out
 
 
 @pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: s.name)
 def test_random_layer_parity(shape):
     lay, inp, cap = _run(shape)
-    check_layer(lay, inp, shape.K, shape.sub_seq, cap, 2e-2)
+    check_layer(lay, inp, shape.K, shape.sub_seq, cap, 1e-5 if shape.dtype == "f32" else 2e-2)
 
 
 def test_user_stream_matches_default_stream():
