@@ -57,6 +57,7 @@
 // as one persistent block per CU that carries the operand ring from tile to tile
 // (gg_wgrad_kernel).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "tile_map.h"
@@ -357,20 +358,30 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
             if (grp == 1) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
 
-            for (int kt = 0; kt < nk; ++kt) {
-                const bool pair_end = (kt & 1) && (kt >> 1) + 1 < np;  // pair kt/2 + 1 due next
+            // One k-step.  KIND 0: any k-step, every condition evaluated at run time; KIND 1
+            // and 2: the even and odd k-step of a pair p with 1 <= p and p + 2 < np, whose
+            // refills (group 0 loads pair p + 1 in the even one, group 1 pair p + 2 in the
+            // odd one) and waits are fixed.  G: this wave's group when known at compile time
+            // (the lean pairs run as one copy per group, so they carry no branches), else -1.
+            auto kstep = [&](int kt, auto kindc, auto grpc) {
+                constexpr int KIND = decltype(kindc)::value;
+                constexpr int G = decltype(grpc)::value;
+                const int g = G < 0 ? grp : G;
+                const bool pair_end = KIND == 1 ? false : KIND == 2 ? true
+                                    : ((kt & 1) && (kt >> 1) + 1 < np);  // pair kt/2 + 1 due next
                 // ---- memory phase
                 read_step(kt);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (grp == 1 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (g == 1 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- compute phase
                 __builtin_amdgcn_s_setprio(1);
-                const int pi = grp == 0 ? ((kt & 1) == 0 && kt >= 2 ? (kt >> 1) + 1 : np)
-                                        : ((kt & 1) ? ((kt + 1) >> 1) + 1 : np);
-                const bool refill = pi < np;
+                const int pi = KIND == 1 ? (kt >> 1) + 1 : KIND == 2 ? ((kt + 1) >> 1) + 1
+                             : g == 0 ? ((kt & 1) == 0 && kt >= 2 ? (kt >> 1) + 1 : np)
+                                      : ((kt & 1) ? ((kt + 1) >> 1) + 1 : np);
+                const bool refill = KIND == 1 ? g == 0 : KIND == 2 ? g == 1 : pi < np;
     #pragma unroll
                 for (int q = 0; q < 32; ++q) {
                     // snake order: consecutive MFMAs differ in one operand only (the
@@ -385,11 +396,29 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
                     }
                 }
                 __builtin_amdgcn_s_setprio(0);
-                if (grp == 0 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (g == 0 && pair_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            using general = std::integral_constant<int, 0>;
+            using even = std::integral_constant<int, 1>;
+            using odd = std::integral_constant<int, 2>;
+            // the whole k-loop runs as one copy per group
+            auto kloop = [&](auto gc) {
+                int kt = 0;
+                for (; kt < min(nk, 2); ++kt) kstep(kt, general{}, gc);
+                if (np >= 4) {
+                    for (int p = 1; p + 2 < np; ++p) {
+                        kstep(2 * p, even{}, gc);
+                        kstep(2 * p + 1, odd{}, gc);
+                    }
+                    kt = 2 * (np - 2);
+                }
+                for (; kt < nk; ++kt) kstep(kt, general{}, gc);
+            };
+            if (grp == 0) kloop(std::integral_constant<int, 0>{});
+            else kloop(std::integral_constant<int, 1>{});
             if (grp == 0) __builtin_amdgcn_s_barrier();
         }
     } else {
@@ -549,17 +578,23 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
             if (grp == 1) __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
 
-            for (int kt = 0; kt < nk; ++kt) {
+            // LEAN: a k-step whose refill target kt + 3 exists (kt + 3 < nk); its waits are
+            // then fixed and its loads unconditional, so the steady state has no branches.
+            auto kstep = [&](int kt, auto lean) {
+                constexpr bool LEAN = decltype(lean)::value;
                 // ---- memory phase
                 read_stage(smem_base + (kt & (STEP_STAGES - 1)) * STEP_STAGE_BYTES);
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (grp == 1) wait_next(kt, 1);
+                if (grp == 1) {
+                    if (LEAN) wait_loads(1);
+                    else wait_next(kt, 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 // ---- compute phase
                 __builtin_amdgcn_s_setprio(1);
-                const bool refill = kt + 3 < nk;
+                const bool refill = LEAN || kt + 3 < nk;
                 const int st3 = (kt + 3) & (STEP_STAGES - 1);
     #pragma unroll
                 for (int q = 0; q < 4 * RB; ++q) {
@@ -585,11 +620,17 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
                     }
                 }
                 __builtin_amdgcn_s_setprio(0);
-                if (grp == 0) wait_next(kt, 2);
+                if (grp == 0) {
+                    if (LEAN) wait_loads(2);
+                    else wait_next(kt, 2);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            int kt = 0;
+            for (; kt + 3 < nk; ++kt) kstep(kt, std::integral_constant<bool, true>{});
+            for (; kt < nk; ++kt) kstep(kt, std::integral_constant<bool, false>{});
             if (grp == 0) __builtin_amdgcn_s_barrier();
         }
     }
@@ -974,18 +1015,24 @@ gg_wgrad_kernel(GemmArgs g) {
                 tnb = ((int64_t)nxt.nrows - (int64_t)(3 - nk) * BK) * ld * 2;
                 tcol2 = (uint32_t)ncol * 2;
             }
-            for (int kt = 0; kt < nk; ++kt) {
+            // One k-step: memory phase, then compute phase.  LEAN: a k-step whose target
+            // kt + 3 and next target kt + 4 both lie in this tile and which no store of the
+            // previous epilogue precedes (2 <= kt, kt + 4 < nk): the waits and the refill
+            // are then fixed, and the steady state carries no branches beyond the one-tile
+            // kernel's.
+            auto kstep = [&](int kt, auto lean) {
+                constexpr bool LEAN = decltype(lean)::value;
                 // ---- memory phase
                 read_stage(smem_base + ((g0 + kt) & (STEP_STAGES - 1)) * STEP_STAGE_BYTES);
-                const bool refill = tvalid;
+                const bool refill = LEAN || tvalid;
                 const uint64_t rbase = tbase;
                 const uint32_t rbytes = tnb >= (int64_t)0xFFFFFFF0 ? 0xFFFFFFF0u : (uint32_t)tnb;
                 const uint32_t rcol2 = tcol2;
                 const uint32_t rdst = smem_base + ((g0 + kt + 3) & (STEP_STAGES - 1)) * STEP_STAGE_BYTES +
                                       grp * STEP_TILE_BYTES + wq * 4 * 1024;
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (grp == 1 && kt + 1 < nk) {
-                    if (kt >= 2 && kt + 2 < nk) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                if (grp == 1 && (LEAN || kt + 1 < nk)) {
+                    if (LEAN || (kt >= 2 && kt + 2 < nk)) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
                     else wait_vm(4 * issued(kt + 2) + held(kt + 1));
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -1006,7 +1053,7 @@ gg_wgrad_kernel(GemmArgs g) {
                 }
                 __builtin_amdgcn_s_setprio(0);
                 // the next target, kt + 4: this tile's k-step, or the next tile's
-                if (kt + 4 < nk) {
+                if (LEAN || kt + 4 < nk) {
                     tbase += kstride;
                     tnb -= kbytes;
                 } else if (kt + 4 == nk) {
@@ -1019,14 +1066,21 @@ gg_wgrad_kernel(GemmArgs g) {
                     tbase += kstride;
                     tnb -= kbytes;
                 }
-                if (grp == 0 && kt + 1 < nk) {
-                    if (kt >= 2 && kt + 3 < nk) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+                if (grp == 0 && (LEAN || kt + 1 < nk)) {
+                    if (LEAN || (kt >= 2 && kt + 3 < nk)) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
                     else wait_vm(4 * (issued(kt + 2) + issued(kt + 3)) + held(kt + 1));
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            };
+            using lean = std::integral_constant<bool, true>;
+            using general = std::integral_constant<bool, false>;
+            const int head = min(nk, 2);
+            int kt = 0;
+            for (; kt < head; ++kt) kstep(kt, general{});
+            for (; kt + 4 < nk; ++kt) kstep(kt, lean{});
+            for (; kt < nk; ++kt) kstep(kt, general{});
             if (grp == 0) __builtin_amdgcn_s_barrier();
         }
 
