@@ -103,8 +103,8 @@ CASES = {
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
     # tile order per segment
     "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),
-    # 2f bytes a multiple of 32 KB: the gate/up dgrad stages pairs of k-steps (every other
-    # case here takes the single-k-step ring)
+    # f = 16384: the dgrads' pairs of k-steps at a 32 KB row pitch and a gate/up dgrad K of
+    # 32768 (512 pairs), as in the Mixtral-8x22B shape
     "paired_dgrad": _shape("paired_dgrad", T=384, d=512, E=2, K=1, f=16384, sub_seq=384, seed=27,
                            w_std=0.02),
     # the permute backward's two forms at their boundary: E = 15 with a shared expert fills

@@ -35,11 +35,11 @@
 // applied by choosing which global chunk each lane fetches, since a direct load
 // writes its 64 lanes' 16 bytes to 1 KB of consecutive LDS.
 //
-// Staging.  Every pass uses a 4-stage ring of single k-steps (32 KB each, three k-steps
-// in flight), except the gate/up dgrad when its operands' rows (both K-major) are a
-// multiple of 32 KB apart: it then loads pairs of k-steps into two 64 KB slots, so that
-// a K-major row is 128 bytes and every load instruction reads whole cache lines (with
-// single k-steps, 16 rows of 64 bytes 32 KB apart per instruction, it ran 16-31% slower).
+// Staging.  The forward passes and the weight gradients use a 4-stage ring of single
+// k-steps (32 KB each, three k-steps in flight).  The two dgrads, whose operands are both
+// K-major, load pairs of k-steps into two 64 KB slots instead, so that a K-major row is
+// 128 bytes and every load instruction reads whole cache lines (with single k-steps an
+// instruction reads 16 rows of 64 bytes).
 //
 // Schedule (ping-pong).  Waves w and w + 4 share a SIMD.  Waves 0-3 and waves 4-7 run
 // the same sequence -- memory phase M(k): read every fragment of k-step k from LDS;
@@ -175,16 +175,17 @@ __device__ __forceinline__ float fast_sigmoid(float a) {
     return __builtin_amdgcn_rcpf(1.0f + __expf(-a));
 }
 
-// PAIRED (gate/up dgrad only): stage pairs of k-steps, so that every direct-load
-// instruction reads whole 128-byte lines (a K-major k-step row is only 64 bytes).  The
-// launch picks it when the operands' row pitch, 2f bytes, is a multiple of 32 KB: there
-// single k-steps (16 rows of 64 bytes per load instruction, rows 32 KB apart) ran 16-31%
-// slower; at every other pitch measured (4, 5, 16, 40, 56 KB) they ran 1-7% faster.
+// PAIRED (the two dgrads): stage pairs of k-steps, so that every direct-load instruction
+// reads whole 128-byte lines (a K-major k-step row is only 64 bytes).  With branch-free
+// steady-state k-steps in both schemes, pairs ran 2-8% faster than single k-steps on every
+// layer shape measured (row pitches 4 to 112 KB), also against the half-height last tiles
+// of the short-segment shapes.
 template <int MODE, bool PAIRED> struct Traits {
     static constexpr bool a_mn = MODE == GG_WGRAD_DOWN || MODE == GG_WGRAD_GATEUP;
     static constexpr bool b_mn = MODE == GG_FWD_GATEUP || MODE == GG_FWD_DOWN || a_mn;
     static constexpr bool paired = PAIRED;
-    static_assert(!PAIRED || MODE == GG_DGRAD_GATEUP, "only the gate/up dgrad stages pairs");
+    static_assert(!PAIRED || MODE == GG_DGRAD_GATEUP || MODE == GG_DGRAD_DOWN,
+                  "the dgrads stage pairs");
 };
 
 // Buffer resource over the raw byte range [base, base + bytes): a direct load through it
@@ -270,26 +271,30 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
     if constexpr (MODE == GG_DGRAD_DOWN) load_x(0, 0);
 
     if constexpr (TR::paired) {
-        static_assert(MODE == GG_DGRAD_GATEUP, "the paired staging serves the gate/up dgrad");
+        static_assert(MODE == GG_DGRAD_GATEUP || MODE == GG_DGRAD_DOWN, "the paired staging serves the dgrads");
         // ---- direct loads.  K-steps are loaded in pairs (64 k) into two 64 KB slots
         // [A 32 KB | B 32 KB]; group 0 loads A, group 1 loads B, and wave wq of a group issues
         // instructions 8wq .. 8wq+7 of the 32 (1 KB each) that cover one operand of a pair.
         // An operand sits as [256 rows][64 k] with 128-byte rows, so that every instruction
         // reads whole 128-byte lines: instruction ii covers rows 8ii + lane/8, physical chunk
         // lane%8 (swizzle chunk ^ ((row >> 1) & 7)).  Every load goes through a buffer
-        // resource whose base moves with the pair (kbase0 + p * kstride, switching to kbase1
-        // at k = f: da with W_g, then db with W_u) and a fixed per-lane byte offset.
-        const int64_t ld = f;  // row pitch of both operands
+        // resource whose base moves with the pair (kbase0 + p * kstride; the gate/up dgrad
+        // switches to kbase1 at k = f: da with W_g, then db with W_u) and a fixed per-lane
+        // byte offset.  Down dgrad: A = d_o rows and B = W_d,e rows n0.., both [.][d].
+        const int64_t ld = MODE == GG_DGRAD_DOWN ? d : f;  // row pitch of both operands
         uint64_t kbase0, kbase1;
         if (grp == 0) {
             kbase0 = (uint64_t)(A0 + (int64_t)m0 * ld);
-            kbase1 = (uint64_t)(A1 + (int64_t)m0 * ld);
+            kbase1 = MODE == GG_DGRAD_DOWN ? kbase0 : (uint64_t)(A1 + (int64_t)m0 * ld);
+        } else if (MODE == GG_DGRAD_DOWN) {
+            kbase0 = (uint64_t)(B0 + (int64_t)e * f * d + (int64_t)n0 * d);
+            kbase1 = kbase0;
         } else {
             kbase0 = (uint64_t)(B0 + (int64_t)e * d * f + (int64_t)n0 * f);
             kbase1 = (uint64_t)(B1 + (int64_t)e * d * f + (int64_t)n0 * f);
         }
         const uint64_t kstride = (uint64_t)KP * 2;
-        const int psplit = f / KP;
+        const int psplit = MODE == GG_DGRAD_DOWN ? 0x7FFFFFFF : f / KP;
         const int np = (nk + 1) >> 1;
         uint32_t voff[8];
     #pragma unroll
@@ -1152,9 +1157,10 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const unsigned G = (unsigned)g8;
     // Short segments (at most 640 rows per expert by the buffer bound) leave many experts
-    // a last row tile of at most 128 rows: the row passes then take the kernel that runs
-    // such a tile at half height, and the weight gradients (whose tiles then have few
+    // a last row tile of at most 128 rows: the forward passes then take the kernel that
+    // runs such a tile at half height, and the weight gradients (whose tiles then have few
     // k-steps) the persistent kernel.  Longer segments keep the one-tile-per-block kernels.
+    // The dgrads stage pairs of k-steps on every shape (full-height tiles).
     const bool half = (int64_t)a.R <= 640LL * a.E;
     switch (mode) {
         case GG_FWD_GATEUP:
@@ -1164,12 +1170,9 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
             return half ? launch_mode<GG_FWD_DOWN, false, true>(a, G, s)
                         : launch_mode<GG_FWD_DOWN>(a, G, s);
         case GG_DGRAD_DOWN:
-            return half ? launch_mode<GG_DGRAD_DOWN, false, true>(a, G, s)
-                        : launch_mode<GG_DGRAD_DOWN>(a, G, s);
+            return launch_mode<GG_DGRAD_DOWN, true>(a, G, s);
         case GG_DGRAD_GATEUP:
-            if (((int64_t)a.f * 2) % 32768 == 0) return launch_mode<GG_DGRAD_GATEUP, true>(a, G, s);
-            return half ? launch_mode<GG_DGRAD_GATEUP, false, true>(a, G, s)
-                        : launch_mode<GG_DGRAD_GATEUP, false>(a, G, s);
+            return launch_mode<GG_DGRAD_GATEUP, true>(a, G, s);
         case GG_WGRAD_DOWN:
         default: {
             if (!half) {
