@@ -894,6 +894,9 @@ __device__ __forceinline__ void wait_vm(int n) {
     }
 }
 
+// Experts a persistent weight-gradient launch can take (the library's limit on E).
+constexpr int WG_MAX_E = 64;
+
 struct WgTile {
     int e, m0, n0, k_lo, nrows, nk;
     bool ok;
@@ -940,12 +943,14 @@ gg_wgrad_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) b_rd[j] = addr_mn(STEP_TILE_BYTES, wn * 64 + j * 16, lane);
 
-    // The segment offsets are read with scalar loads (through the constant address
-    // space): a vector load here would be followed by a wait for every vector memory
-    // operation in flight, the previous epilogue's stores and the prefetched k-steps
-    // included.
-    typedef const __attribute__((address_space(4))) int32_t const_i32;
-    const_i32* offs = (const_i32*)g.offsets;
+    // The segment offsets (E + 1 <= WG_MAX_E + 1 values) are staged in LDS once, so that
+    // a tile's decode reads them with LDS loads: a vector load at a tile boundary would
+    // be followed by a wait for every vector memory operation in flight (the previous
+    // epilogue's stores and the prefetched k-steps included), and a scalar load there
+    // measured 0.4 µs of latency under this kernel's memory traffic.
+    __shared__ int32_t offs_lds[WG_MAX_E + 1];
+    if (tid <= g.E) offs_lds[tid] = g.offsets[tid];
+    __syncthreads();
     auto decode = [&](int64_t b) {
         WgTile t{0, 0, 0, 0, 0, 0, false};
         int e, mi, ni;
@@ -955,8 +960,8 @@ gg_wgrad_kernel(GemmArgs g) {
         t.e = e;
         t.m0 = __builtin_amdgcn_readfirstlane(mi) * BM;
         t.n0 = __builtin_amdgcn_readfirstlane(ni) * BN;
-        t.k_lo = offs[e];
-        t.nrows = offs[e + 1] - t.k_lo;
+        t.k_lo = __builtin_amdgcn_readfirstlane(offs_lds[e]);
+        t.nrows = __builtin_amdgcn_readfirstlane(offs_lds[e + 1]) - t.k_lo;
         t.nk = (t.nrows + BK - 1) / BK;
         return t;
     };
@@ -1210,6 +1215,7 @@ hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
             }
             // short segments (few k-steps per tile): one persistent block per CU (at most
             // one fits: 128 KB of LDS), walking the same tiles as the G one-tile blocks
+            if (a.E > WG_MAX_E) return hipErrorInvalidValue;
             int dev = 0, cus = 0;
             hipError_t err = hipGetDevice(&dev);
             if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
