@@ -47,7 +47,11 @@
 // loads between them -- one phase apart, separated by block barriers, so that on
 // every SIMD one wave issues MFMAs while the other reads LDS.  The LDS reads of one
 // phase take about as long as its MFMAs, and the direct loads are issued by the
-// computing wave, where their issue cost hides under the MFMA pipeline.
+// computing wave, where their issue cost hides under the MFMA pipeline.  Every k-loop
+// runs its steady-state k-steps (refill target in range, fixed wait counts) as a
+// separate copy of the loop body with unconditional loads and constant waits, and the
+// dgrads and forward passes run one copy of the loop per wave group: the loop's own
+// branches cost 2-7% per pass.
 //
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
 // that each XCD runs a contiguous range, in which consecutive tiles form 4 x 8 blocks
