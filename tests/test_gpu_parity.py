@@ -103,6 +103,13 @@ CASES = {
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped
     # tile order per segment
     "two_long": _shape("two_long", T=1024, d=512, E=2, K=2, f=768, seed=30, w_std=0.05),
+    # more than 640 rows per expert: the weight gradients take the one-tile-per-block kernel
+    # (every shorter case here takes the persistent one); one expert, and three with a
+    # ragged last k-step
+    "onetile_e1": _shape("onetile_e1", T=768, d=256, E=1, K=1, f=512, sub_seq=768, seed=38,
+                         w_std=0.05),
+    "onetile_e3": _shape("onetile_e3", T=1000, d=512, E=3, K=2, f=256, sub_seq=1000, seed=39,
+                         w_std=0.05),
     # f = 16384: the dgrads' pairs of k-steps at a 32 KB row pitch and a gate/up dgrad K of
     # 32768 (512 pairs), as in the Mixtral-8x22B shape
     "paired_dgrad": _shape("paired_dgrad", T=384, d=512, E=2, K=1, f=16384, sub_seq=384, seed=27,
