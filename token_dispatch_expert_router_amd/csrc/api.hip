@@ -89,6 +89,8 @@ size_t esize(const moe_desc& d) { return d.dtype == MOE_BF16 ? 2 : 4; }
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 
+// Route workspace: per-group kept counts, kept lists, and the router weight (plus the
+// shared-expert gate column) rewritten in matrix-core fragment order for the router GEMM.
 struct RouteLayout {
     size_t kcnt, list, wrt, total;
 };
@@ -191,8 +193,8 @@ moe_status route_launch(const moe_desc& d, const void* x, const void* w_router, 
 // Route scratch of moe_route_noalloc: one copy per GPU, held until the process ends.
 // Every call on a GPU reuses that GPU's copy (calls that overlap on one GPU race).
 // Nothing in it has to start at zero: the select kernels write every per-group count
-// and the kept lists before the maps kernel reads them, and the transposed router
-// weight is rewritten by each call.
+// and the kept lists before the maps kernel reads them, and the router weight in
+// matrix-core fragment order is rewritten by each call.
 static __device__ __align__(256) char scratch[MOE_ROUTE_SCRATCH_BYTES];
 
 constexpr int kMaxDevices = 64;
