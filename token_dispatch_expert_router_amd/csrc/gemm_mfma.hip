@@ -379,8 +379,8 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
             // One k-step.  KIND 0: any k-step, every condition evaluated at run time; KIND 1
             // and 2: the even and odd k-step of a pair p with 1 <= p and p + 2 < np, whose
             // refills (group 0 loads pair p + 1 in the even one, group 1 pair p + 2 in the
-            // odd one) and waits are fixed.  G: this wave's group when known at compile time
-            // (the lean pairs run as one copy per group, so they carry no branches), else -1.
+            // odd one) and waits are fixed.  G: this wave's group, a compile-time constant
+            // (the k-loop runs as one copy per group, so the lean pairs carry no branches).
             auto kstep = [&](int kt, auto kindc, auto grpc) {
                 constexpr int KIND = decltype(kindc)::value;
                 constexpr int G = decltype(grpc)::value;
@@ -422,7 +422,6 @@ __device__ __forceinline__ void gg_tile(const GemmArgs& g, uint32_t smem_base, i
             using general = std::integral_constant<int, 0>;
             using even = std::integral_constant<int, 1>;
             using odd = std::integral_constant<int, 2>;
-            // the whole k-loop runs as one copy per group
             auto kloop = [&](auto gc) {
                 int kt = 0;
                 for (; kt < min(nk, 2); ++kt) kstep(kt, general{}, gc);
