@@ -288,7 +288,10 @@ def _random_shapes(n=24, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: s.name)
+# MOE_PARITY_RANDOM / MOE_PARITY_SEED widen the sweep (default 24 layers, seed 2024)
+@pytest.mark.parametrize("shape", _random_shapes(int(os.environ.get("MOE_PARITY_RANDOM", "24")),
+                                                 int(os.environ.get("MOE_PARITY_SEED", "2024"))),
+                         ids=lambda s: s.name)
 def test_random_layer_parity(shape):
     lay, inp, cap = _run(shape)
     check_layer(lay, inp, shape.K, shape.sub_seq, cap, 1e-5 if shape.dtype == "f32" else 2e-2)
