@@ -288,6 +288,36 @@ def _random_shapes(n=24, seed=2024):
     return out
 
 
+def _medium_shapes(n=8, seed=4242):
+    """Seeded random medium layers: 256-1279-token sub-sequences, one or two of them, d up
+    to 1024, f up to 1024, 1 to 16 experts, K up to 4, dropless or cf in [0.5, 1.5], an
+    optional shared expert: segments of several row tiles, several n-tiles, and the
+    one-tile weight-gradient kernel whenever an expert gets more than 640 rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([256, 512, 768, 1024]))
+        f = int(rng.choice([256, 512, 1024]))
+        E = int(rng.choice([1, 2, 4, 8, 16]))
+        K = int(rng.integers(1, min(E, 4) + 1))
+        n_sub = int(rng.integers(1, 3))
+        S = int(rng.integers(256, 1280))
+        cf = None if rng.random() < 0.4 else float(np.round(rng.uniform(0.5, 1.5), 2))
+        fs = int(rng.choice([0, 0, 0, 512]))
+        out.append(_shape(f"med{i}", T=n_sub * S, d=d, E=E, K=K, f=f, sub_seq=S, cf=cf, fs=fs,
+                          seed=5000 + i, w_std=0.03, wr_std=0.5))
+    return out
+
+
+# MOE_PARITY_MEDIUM / MOE_PARITY_SEED widen this sweep (default 8 layers, seed 4242)
+@pytest.mark.parametrize("shape", _medium_shapes(int(os.environ.get("MOE_PARITY_MEDIUM", "8")),
+                                                 int(os.environ.get("MOE_PARITY_SEED", "4242"))),
+                         ids=lambda s: s.name)
+def test_medium_layer_parity(shape):
+    lay, inp, cap = _run(shape)
+    check_layer(lay, inp, shape.K, shape.sub_seq, cap, 2e-2)
+
+
 # MOE_PARITY_RANDOM / MOE_PARITY_SEED widen the sweep (default 24 layers, seed 2024)
 @pytest.mark.parametrize("shape", _random_shapes(int(os.environ.get("MOE_PARITY_RANDOM", "24")),
                                                  int(os.environ.get("MOE_PARITY_SEED", "2024"))),
