@@ -4,12 +4,16 @@
 //   - row passes, with and without half-height last tiles: the grid holds every real
 //     tile; each block maps to at most one tile, which lies inside one segment (first row
 //     in [lo, hi), tile-aligned from lo, limit hi, a 128-row tile only as a segment's
-//     last tile reaching its end) with an n-tile in range; each XCD (block b on XCD b % 8) runs one contiguous
-//     range of logical tiles; every (expert, m-tile, n-tile) is produced exactly once;
+//     last tile reaching its end) with an n-tile in range; every (expert, m-tile, n-tile)
+//     is produced exactly once; with the contiguous map each XCD (block b on XCD b % 8)
+//     runs one contiguous range of the logical tile order, with the shared map it gets the
+//     same share of every expert's tiles to within one, one contiguous range of each
+//     expert's tile order, expert by expert;
 //   - weight gradients: every (expert, m-tile, n-tile) exactly once, and each XCD gets
 //     the same share of every expert's tiles to within one.
 // Usage: tile_map_check E R d f off_0 ... off_E   (prints one line per pass; exit 1 on
 // the first violation).
+#include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -24,27 +28,37 @@ static int fail(const char* pass, const char* what, long a, long b, long c) {
     return 1;
 }
 
+// Position of (m-tile mi, n-tile ni) in a segment's grouped tile order (the inverse of
+// tiles::grouped_mn).
+static int grouped_pos(int mi, int ni, int mt, int n_tiles) {
+    const int gi = mi / tiles::GROUP_M;
+    const int rest = mt - gi * tiles::GROUP_M;
+    const int gm = rest < tiles::GROUP_M ? rest : tiles::GROUP_M;
+    return gi * tiles::GROUP_M * n_tiles + ni * gm + (mi - gi * tiles::GROUP_M);
+}
+
+// The map each launch takes is tiles::row_share(mode, R, E), and the grid is sized for
+// it; the other map is walked over the same grid only where that grid has room for it
+// (the shared map needs up to E more blocks per XCD).
 static int check_rows(int mode, const char* name, const std::vector<int32_t>& off, int E, int64_t R,
-                      int d, int f, bool half) {
+                      int d, int f, bool half, bool share) {
     const int nt_n = tiles::row_n_tiles(mode, d, f);
-    const int64_t G = tiles::grid_blocks(mode, E, R, d, f);
+    int64_t G = tiles::grid_blocks(mode, E, R, d, f);
+    if (share && !tiles::row_share(mode, R, E)) G += 8LL * E;
     const int valid = tiles::count_row_tiles(off.data(), E) * nt_n;
     if (G % 8 != 0) return fail(name, "grid not a multiple of 8", G, 0, 0);
-    // every real tile has a block: the largest block index xcd_remap can use
-    const int per = (valid + 7) / 8;
-    if ((int64_t)per * 8 > G && valid > 0) return fail(name, "grid too small", G, valid, per);
     std::vector<int> seen;
     std::vector<int64_t> base(E + 1, 0);
     for (int e = 0; e < E; ++e)
         base[e + 1] = base[e] + (int64_t)((off[e + 1] - off[e] + tiles::BM - 1) / tiles::BM) * nt_n;
     seen.assign((size_t)base[E], 0);
-    std::vector<int> lo_L(8, 1 << 30), hi_L(8, -1), n_L(8, 0);
+    std::vector<int> share_n((size_t)E * 8, 0), last_e(8, -1);
+    std::vector<int64_t> lo_L(8, INT64_MAX), hi_L(8, -1), n_L(8, 0);
+    std::vector<int> lo_p((size_t)E * 8, 1 << 30), hi_p((size_t)E * 8, -1);
     for (int64_t b = 0; b < G; ++b) {
-        const int L = tiles::xcd_remap((int)b, valid);
-        if (L < 0) continue;
         int e, m0, m_lim, nt, mh;
-        if (!tiles::decode_rows(L, off.data(), E, nt_n, half, e, m0, m_lim, nt, mh))
-            return fail(name, "decode failed for a valid tile", b, L, valid);
+        if (!tiles::row_tile((int)b, off.data(), E, nt_n, half, share, e, m0, m_lim, nt, mh)) continue;
+        if (e < 0 || e >= E) return fail(name, "expert out of range", b, e, E);
         const int lo = off[e], hi = off[e + 1];
         if (!(m0 >= lo && m0 < hi)) return fail(name, "first row outside its segment", e, m0, lo);
         // a tile covers rows [m0, min(m0 + mh, hi)); a half-height tile must reach the
@@ -55,18 +69,43 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
         if (m_lim != hi || hi > R) return fail(name, "row limit", e, m_lim, hi);
         if (nt < 0 || nt >= nt_n) return fail(name, "n-tile out of range", e, nt, nt_n);
         const int x = (int)(b % 8);
+        const int mi = (m0 - lo) / tiles::BM, mt = (hi - lo + tiles::BM - 1) / tiles::BM;
+        const int pos = grouped_pos(mi, nt, mt, nt_n);
+        const int64_t L = base[e] + pos;
         lo_L[x] = L < lo_L[x] ? L : lo_L[x];
         hi_L[x] = L > hi_L[x] ? L : hi_L[x];
         n_L[x]++;
-        const int64_t id = base[e] + (int64_t)((m0 - lo) / tiles::BM) * nt_n + nt;
+        const size_t ex = (size_t)e * 8 + x;
+        lo_p[ex] = pos < lo_p[ex] ? pos : lo_p[ex];
+        hi_p[ex] = pos > hi_p[ex] ? pos : hi_p[ex];
+        if (share && e < last_e[x]) return fail(name, "an XCD's tiles are not expert by expert", x, e, last_e[x]);
+        last_e[x] = e;
+        share_n[ex]++;
+        const int64_t id = base[e] + (int64_t)mi * nt_n + nt;
         if (++seen[(size_t)id] != 1) return fail(name, "tile produced twice", e, m0, nt);
     }
     for (size_t i = 0; i < seen.size(); ++i)
         if (seen[i] != 1) return fail(name, "tile never produced", (long)i, (long)seen.size(), 0);
-    for (int x = 0; x < 8; ++x)
-        if (n_L[x] && hi_L[x] - lo_L[x] + 1 != n_L[x])
-            return fail(name, "an XCD's tiles are not one contiguous range", x, lo_L[x], hi_L[x]);
-    printf("%s%s blocks %lld tiles %d ok\n", name, half ? " (half tiles)" : "", (long long)G, valid);
+    if (!share) {
+        for (int x = 0; x < 8; ++x)
+            if (n_L[x] && hi_L[x] - lo_L[x] + 1 != n_L[x])
+                return fail(name, "an XCD's tiles are not one contiguous range", x, (long)lo_L[x], (long)hi_L[x]);
+    } else {
+        for (int e = 0; e < E; ++e) {
+            int mn = 1 << 30, mx = 0;
+            for (int x = 0; x < 8; ++x) {
+                const size_t ex = (size_t)e * 8 + x;
+                const int v = share_n[ex];
+                mn = v < mn ? v : mn;
+                mx = v > mx ? v : mx;
+                if (v && hi_p[ex] - lo_p[ex] + 1 != v)
+                    return fail(name, "an XCD's share of an expert is not contiguous", e, x, v);
+            }
+            if (mx - mn > 1) return fail(name, "uneven XCD share of an expert", e, mn, mx);
+        }
+    }
+    printf("%s%s%s blocks %lld tiles %d ok\n", name, half ? " (half tiles)" : "",
+           share ? " (shared map)" : " (contiguous map)", (long long)G, valid);
     return 0;
 }
 
@@ -136,12 +175,13 @@ int main(int argc, char** argv) {
         if (off[i + 1] < off[i]) return fail("input", "offsets decrease", i, off[i], off[i + 1]);
     if (off[E] > R) return fail("input", "offsets[E] > R", off[E], R, 0);
     int rc = 0;
-    for (int h = 0; h < 2; ++h) {
-        rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f, h == 1);
-        rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f, h == 1);
-        rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f, h == 1);
-        rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f, h == 1);
-    }
+    for (int h = 0; h < 2; ++h)
+        for (int sh = 0; sh < 2; ++sh) {
+            rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f, h == 1, sh == 1);
+            rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f, h == 1, sh == 1);
+            rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f, h == 1, sh == 1);
+            rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f, h == 1, sh == 1);
+        }
     rc |= check_wgrad(GG_WGRAD_DOWN, "wgrad_down", E, R, d, f);
     rc |= check_wgrad(GG_WGRAD_GATEUP, "wgrad_gateup", E, R, d, f);
     return rc;

@@ -54,12 +54,13 @@
 // branches cost 2-7% per pass.
 //
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
-// that each XCD runs a contiguous range, in which consecutive tiles form 4 x 8 blocks
-// (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2.  The
-// weight-gradient passes, whose tiles' K is their expert's segment length, give each
-// XCD an equal contiguous share of every expert instead; with short segments they run
-// as one persistent block per CU that carries the operand ring from tile to tile
-// (gg_wgrad_kernel).
+// that each XCD runs contiguous runs of tiles, in which consecutive tiles form 4 x 8
+// blocks (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2:
+// either one contiguous eighth of all tiles or the same contiguous eighth of every
+// expert's tiles, chosen per launch by measurement (tiles::row_share).  The
+// weight-gradient passes, whose tiles' K is their expert's segment length, always take
+// the latter; with short segments they run as one persistent block per CU that carries
+// the operand ring from tile to tile (gg_wgrad_kernel).
 #include <algorithm>
 #include <type_traits>
 
@@ -88,9 +89,6 @@ constexpr int KP = 2 * BK;                              // k of one pair
 constexpr int OP_BYTES = BM * KP * 2;                   // one operand of one pair: 32 KB
 constexpr int SLOT_BYTES = 2 * OP_BYTES;                // A and B of one pair: 64 KB
 
-using tiles::xcd_remap;
-using tiles::count_row_tiles;
-using tiles::decode_rows;
 
 // Swizzles.  K-major pair tile [256 rows][64 k] (128-byte rows): physical chunk p of
 // row r holds logical chunk p ^ ((r >> 1) & 7); a ds_read_b128 is served 16 consecutive
@@ -835,11 +833,10 @@ gg_mfma_kernel(GemmArgs g) {
     bool half = false;
     if (MODE <= GG_DGRAD_GATEUP) {
         const int n_tiles = tiles::row_n_tiles(MODE, d, f);
-        // only the tiles the segments have are spread over the XCDs
-        const int L = xcd_remap(blockIdx.x, count_row_tiles(g.offsets, g.E) * n_tiles);
-        if (L < 0) return;
         int nt, mh;
-        if (!decode_rows(L, g.offsets, g.E, n_tiles, HALF, e, m0, m_lim, nt, mh)) return;
+        if (!tiles::row_tile(blockIdx.x, g.offsets, g.E, n_tiles, HALF, g.row_share != 0, e, m0,
+                             m_lim, nt, mh))
+            return;
         half = mh < BM;
         n0 = nt * (MODE == GG_FWD_GATEUP ? 128 : BN);
         const int K = MODE == GG_FWD_GATEUP ? d : MODE == GG_FWD_DOWN ? f
@@ -1188,7 +1185,9 @@ bool mfma_shape_ok(const moe_desc& d) {
     return d.dtype == MOE_BF16 && d.d % 256 == 0 && d.f % 256 == 0 && d.d > 0 && d.f > 0;
 }
 
-hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& args, hipStream_t s) {
+    GemmArgs a = args;
+    a.row_share = tiles::row_share(mode, a.R, a.E) ? 1 : 0;
     const int64_t g8 = tiles::grid_blocks(mode, a.E, a.R, a.d, a.f);
     if (g8 <= 0) return hipSuccess;
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

@@ -6,9 +6,9 @@
 // The experts' rows are contiguous segments [offsets[e], offsets[e+1]) of the permuted
 // buffer whose sizes live only in device memory, so a block of a row-segmented pass
 // finds its (expert, m-tile, n-tile) from `offsets` itself.  Blocks are dispatched
-// round-robin over the 8 XCDs (block b runs on XCD b & 7); the maps give each XCD a
-// contiguous range of tiles, in which consecutive tiles form 4 x N blocks (groups of
-// four m-tiles, M fastest) whose operand panels stay in that XCD's L2.
+// round-robin over the 8 XCDs (block b runs on XCD b & 7); the maps give each XCD
+// contiguous runs of tiles, in which consecutive tiles form 4 x N blocks (groups of four
+// m-tiles, M fastest) whose operand panels stay in that XCD's L2.
 #pragma once
 
 #include "common.h"
@@ -21,6 +21,13 @@ constexpr int BN = 256;  // output columns per tile (the gate/up forward: 128 of
 constexpr int GROUP_M = 4;
 constexpr int NXCD = 8;
 
+// Row tiles over all segments.
+__host__ __device__ __forceinline__ int count_row_tiles(const int32_t* offsets, int E) {
+    int mt = 0;
+    for (int i = 0; i < E; ++i) mt += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
+    return mt;
+}
+
 // Logical tile L of `valid` goes to XCD L / ceil(valid / 8), so that each XCD runs a
 // contiguous range of equal length; returns -1 for a block with no tile.
 __host__ __device__ __forceinline__ int xcd_remap(int b, int valid) {
@@ -29,13 +36,6 @@ __host__ __device__ __forceinline__ int xcd_remap(int b, int valid) {
     if (j >= per) return -1;
     const int L = (b % NXCD) * per + j;
     return L < valid ? L : -1;
-}
-
-// Row tiles over all segments (the grid is sized for the worst case, ceil(R/256) + E).
-__host__ __device__ __forceinline__ int count_row_tiles(const int32_t* offsets, int E) {
-    int mt = 0;
-    for (int i = 0; i < E; ++i) mt += (offsets[i + 1] - offsets[i] + BM - 1) / BM;
-    return mt;
 }
 
 // Tiles of one segment (or one expert's weight gradient) are ordered in groups of
@@ -52,30 +52,83 @@ __host__ __device__ __forceinline__ void grouped_mn(int loc, int mt, int n_tiles
     ni = idx / gm;
 }
 
-// (expert, first row, segment end, n-tile, tile height) of logical tile L for passes with
-// segmented rows; false past the last tile.  With `half`, a segment's last row tile is
-// 128 rows high when it holds at most 128 rows (the tile count does not change); every
-// other tile is BM rows high.
-__host__ __device__ __forceinline__ bool decode_rows(int L, const int32_t* offsets, int E,
-                                                     int n_tiles, bool half, int& e, int& m0,
-                                                     int& m_lim, int& nt, int& mh) {
+// (first row, tile height) of m-tile mi of a segment [lo, hi).  With `half`, a segment's
+// last row tile is 128 rows high when it holds at most 128 rows (the tile count does not
+// change); every other tile is BM rows high.
+__host__ __device__ __forceinline__ void row_extent(int lo, int hi, int mi, bool half, int& m0,
+                                                    int& mh) {
+    m0 = lo + mi * BM;
+    mh = (half && hi - m0 <= BM / 2) ? BM / 2 : BM;
+}
+
+// Row passes: (expert, first row, segment end, n-tile, tile height) of block b, false
+// for a block with no tile.  Two maps, chosen per launch (row_share):
+//  - contiguous: the tiles of all segments in order (each segment's in grouped order) are
+//    cut into eight equal contiguous ranges, one per XCD, so an XCD keeps one expert's
+//    row panels to itself;
+//  - shared: XCD x takes the same contiguous eighth of every segment's tile order, tiles
+//    [x T / 8, (x + 1) T / 8) of a segment of T tiles, segment after segment, so all XCDs
+//    work on the same experts at the same time (the weight panels that several XCDs
+//    need are then fetched from HBM once and served to the others by the last-level
+//    cache) and each streams the same share of every expert's weights, however unequal
+//    the segments.
+// Block b runs the (b / 8)-th tile of XCD b % 8's sequence.
+__host__ __device__ __forceinline__ bool row_tile(int b, const int32_t* offsets, int E,
+                                                  int n_tiles, bool half, bool share, int& e,
+                                                  int& m0, int& m_lim, int& nt, int& mh) {
+    int mi;
+    if (!share) {
+        const int L = xcd_remap(b, count_row_tiles(offsets, E) * n_tiles);
+        if (L < 0) return false;
+        int acc = 0;
+        for (int i = 0; i < E; ++i) {
+            const int lo = offsets[i], hi = offsets[i + 1];
+            const int mt = (hi - lo + BM - 1) / BM;
+            const int tiles = mt * n_tiles;
+            if (L < acc + tiles) {
+                grouped_mn(L - acc, mt, n_tiles, mi, nt);
+                e = i;
+                m_lim = hi;
+                row_extent(lo, hi, mi, half, m0, mh);
+                return true;
+            }
+            acc += tiles;
+        }
+        return false;
+    }
+    const unsigned x = (unsigned)b % NXCD;
+    const int j = b / NXCD;
     int acc = 0;
     for (int i = 0; i < E; ++i) {
         const int lo = offsets[i], hi = offsets[i + 1];
         const int mt = (hi - lo + BM - 1) / BM;
-        const int tiles = mt * n_tiles;
-        if (L < acc + tiles) {
-            int mi;
-            grouped_mn(L - acc, mt, n_tiles, mi, nt);
+        const unsigned tiles = (unsigned)(mt * n_tiles);
+        const int t0 = (int)((uint64_t)x * tiles / NXCD);
+        const int cnt = (int)((uint64_t)(x + 1) * tiles / NXCD) - t0;
+        if (j < acc + cnt) {
+            grouped_mn(t0 + (j - acc), mt, n_tiles, mi, nt);
             e = i;
-            m0 = lo + mi * BM;
             m_lim = hi;
-            mh = (half && hi - m0 <= BM / 2) ? BM / 2 : BM;
+            row_extent(lo, hi, mi, half, m0, mh);
             return true;
         }
-        acc += tiles;
+        acc += cnt;
     }
     return false;
+}
+
+// Which row map a launch takes, by measurement on the layer shapes (R rows of buffer
+// bound over E experts): with more than 1024 rows per expert (two or more groups of
+// four m-tiles) the shared map on every row pass (forward and dgrads 4-8% faster: the
+// XCDs that run the same weight columns for different row groups do so at the same
+// time); with 641-1024 rows the shared map on all but the down forward pass (the dgrads
+// 4% faster, the down forward 4% slower); with at most 640 rows (one or two m-tiles per
+// expert, whose row panels the shared map sends to all eight XCDs) only on the gate/up
+// forward pass, whose half-height last tiles otherwise leave the XCDs unequal work (5%).
+__host__ __forceinline__ bool row_share(int mode, int64_t R, int E) {
+    if (mode == GG_FWD_GATEUP) return true;
+    if (mode == GG_FWD_DOWN) return R > 1024LL * E;
+    return R > 640LL * E;
 }
 
 // n-tiles of a row-segmented pass (modes GG_FWD_GATEUP .. GG_DGRAD_GATEUP).
@@ -111,8 +164,9 @@ __host__ __device__ __forceinline__ bool wgrad_tile(int b, int E, int MT, int NT
 }
 
 // Blocks a pass launches (a multiple of 8): row passes are sized for the worst case of
-// ceil(R / 256) + E m-tiles (the real counts live on the device); the weight gradients
-// for ceil(per / 8) tiles of each expert on every XCD.
+// ceil(R / 256) + E m-tiles (the real counts live on the device), with the shared map
+// plus E blocks per XCD for the rounding of each segment's eighth up to whole tiles; the
+// weight gradients for ceil(per / 8) tiles of each expert on every XCD.
 __host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, int f) {
     int64_t tiles;
     if (mode == GG_WGRAD_DOWN || mode == GG_WGRAD_GATEUP) {
@@ -121,7 +175,8 @@ __host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, 
         tiles = (int64_t)E * (((int64_t)MT * NT + NXCD - 1) / NXCD) * NXCD;
     } else {
         const int64_t mt_max = (R + BM - 1) / BM + E;
-        tiles = mt_max * row_n_tiles(mode, d, f);
+        tiles = (mt_max * row_n_tiles(mode, d, f) + NXCD - 1) / NXCD * NXCD;
+        if (row_share(mode, R, E)) tiles += (int64_t)NXCD * E;
     }
     return (tiles + NXCD - 1) / NXCD * NXCD;
 }
