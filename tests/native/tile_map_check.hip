@@ -6,9 +6,10 @@
 //     in [lo, hi), tile-aligned from lo, limit hi, a 128-row tile only as a segment's
 //     last tile reaching its end) with an n-tile in range; every (expert, m-tile, n-tile)
 //     is produced exactly once; with the contiguous map each XCD (block b on XCD b % 8)
-//     runs one contiguous range of the logical tile order, with the shared map it gets the
-//     same share of every expert's tiles to within one, one contiguous range of each
-//     expert's tile order, expert by expert;
+//     runs one contiguous range of the logical tile order, with the chunked map whole
+//     chunks x, x + 8, ... of it, with the shared map the same share of every expert's
+//     tiles to within one, one contiguous range of each expert's tile order, expert by
+//     expert;
 //   - weight gradients: every (expert, m-tile, n-tile) exactly once, and each XCD gets
 //     the same share of every expert's tiles to within one.
 // Usage: tile_map_check E R d f off_0 ... off_E   (prints one line per pass; exit 1 on
@@ -37,14 +38,13 @@ static int grouped_pos(int mi, int ni, int mt, int n_tiles) {
     return gi * tiles::GROUP_M * n_tiles + ni * gm + (mi - gi * tiles::GROUP_M);
 }
 
-// The map each launch takes is tiles::row_share(mode, R, E), and the grid is sized for
-// it; the other map is walked over the same grid only where that grid has room for it
-// (the shared map needs up to E more blocks per XCD).
+// Every map is walked over the grid sized for it (tiles::grid_blocks with that map); the
+// launch takes the one tiles::row_map picks.
 static int check_rows(int mode, const char* name, const std::vector<int32_t>& off, int E, int64_t R,
-                      int d, int f, bool half, bool share) {
+                      int d, int f, bool half, int map) {
     const int nt_n = tiles::row_n_tiles(mode, d, f);
-    int64_t G = tiles::grid_blocks(mode, E, R, d, f);
-    if (share && !tiles::row_share(mode, R, E)) G += 8LL * E;
+    const int64_t G = tiles::grid_blocks(mode, E, R, d, f, map);
+    const bool share = map == tiles::ROW_SHARED;
     const int valid = tiles::count_row_tiles(off.data(), E) * nt_n;
     if (G % 8 != 0) return fail(name, "grid not a multiple of 8", G, 0, 0);
     std::vector<int> seen;
@@ -57,7 +57,7 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
     std::vector<int> lo_p((size_t)E * 8, 1 << 30), hi_p((size_t)E * 8, -1);
     for (int64_t b = 0; b < G; ++b) {
         int e, m0, m_lim, nt, mh;
-        if (!tiles::row_tile((int)b, off.data(), E, nt_n, half, share, e, m0, m_lim, nt, mh)) continue;
+        if (!tiles::row_tile((int)b, off.data(), E, nt_n, half, map, e, m0, m_lim, nt, mh)) continue;
         if (e < 0 || e >= E) return fail(name, "expert out of range", b, e, E);
         const int lo = off[e], hi = off[e + 1];
         if (!(m0 >= lo && m0 < hi)) return fail(name, "first row outside its segment", e, m0, lo);
@@ -72,6 +72,8 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
         const int mi = (m0 - lo) / tiles::BM, mt = (hi - lo + tiles::BM - 1) / tiles::BM;
         const int pos = grouped_pos(mi, nt, mt, nt_n);
         const int64_t L = base[e] + pos;
+        if (map == tiles::ROW_CHUNKED && (L / tiles::CHUNK) % 8 != x)
+            return fail(name, "a chunk on the wrong XCD", x, (long)L, (long)(L / tiles::CHUNK));
         lo_L[x] = L < lo_L[x] ? L : lo_L[x];
         hi_L[x] = L > hi_L[x] ? L : hi_L[x];
         n_L[x]++;
@@ -86,11 +88,11 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
     }
     for (size_t i = 0; i < seen.size(); ++i)
         if (seen[i] != 1) return fail(name, "tile never produced", (long)i, (long)seen.size(), 0);
-    if (!share) {
+    if (map == tiles::ROW_CONTIGUOUS) {
         for (int x = 0; x < 8; ++x)
             if (n_L[x] && hi_L[x] - lo_L[x] + 1 != n_L[x])
                 return fail(name, "an XCD's tiles are not one contiguous range", x, (long)lo_L[x], (long)hi_L[x]);
-    } else {
+    } else if (share) {
         for (int e = 0; e < E; ++e) {
             int mn = 1 << 30, mx = 0;
             for (int x = 0; x < 8; ++x) {
@@ -104,8 +106,9 @@ static int check_rows(int mode, const char* name, const std::vector<int32_t>& of
             if (mx - mn > 1) return fail(name, "uneven XCD share of an expert", e, mn, mx);
         }
     }
-    printf("%s%s%s blocks %lld tiles %d ok\n", name, half ? " (half tiles)" : "",
-           share ? " (shared map)" : " (contiguous map)", (long long)G, valid);
+    static const char* map_name[3] = {" (contiguous map)", " (shared map)", " (chunked map)"};
+    printf("%s%s%s blocks %lld tiles %d ok\n", name, half ? " (half tiles)" : "", map_name[map],
+           (long long)G, valid);
     return 0;
 }
 
@@ -176,11 +179,11 @@ int main(int argc, char** argv) {
     if (off[E] > R) return fail("input", "offsets[E] > R", off[E], R, 0);
     int rc = 0;
     for (int h = 0; h < 2; ++h)
-        for (int sh = 0; sh < 2; ++sh) {
-            rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f, h == 1, sh == 1);
-            rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f, h == 1, sh == 1);
-            rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f, h == 1, sh == 1);
-            rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f, h == 1, sh == 1);
+        for (int map = 0; map < 3; ++map) {
+            rc |= check_rows(GG_FWD_GATEUP, "fwd_gateup", off, E, R, d, f, h == 1, map);
+            rc |= check_rows(GG_FWD_DOWN, "fwd_down", off, E, R, d, f, h == 1, map);
+            rc |= check_rows(GG_DGRAD_DOWN, "dgrad_down", off, E, R, d, f, h == 1, map);
+            rc |= check_rows(GG_DGRAD_GATEUP, "dgrad_gateup", off, E, R, d, f, h == 1, map);
         }
     rc |= check_wgrad(GG_WGRAD_DOWN, "wgrad_down", E, R, d, f);
     rc |= check_wgrad(GG_WGRAD_GATEUP, "wgrad_gateup", E, R, d, f);

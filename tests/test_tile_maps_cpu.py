@@ -1,19 +1,20 @@
 """Host check of the grouped GEMM's tile maps (no GPU).
 
-The functions that pick a block's output tile (csrc/tile_map.h: the two row maps, the
+The functions that pick a block's output tile (csrc/tile_map.h: the three row maps, the
 grouped m/n order and the weight-gradient split) are compiled for the CPU into
 tests/native/tile_map_check, which walks every block of each of the six launches (the
-row passes with and without half-height tiles, under both row maps) and asserts that
+row passes with and without half-height tiles, under each row map) and asserts that
 every output tile is produced exactly once, inside its segment, with each XCD on one
-contiguous range of tiles (contiguous row map) or an equal, contiguous share of every
-expert (shared row map, weight gradients); for the weight gradients it also walks the persistent
-launch (256, 64 or 8 blocks, each stepping through the one-tile launch's blocks of its
-XCD until the first without a tile) and asserts the same exact-once coverage.  Offsets: each bf16 layer shape routed by the oracle
-on router inputs drawn on the CPU (the same recipe and sizes as on the GPU; the CPU
-generator's values differ from the GPU's, so the segments are of the same distribution,
-not identical; the GPU test runs the same check on the device's own offsets), plus
-edge cases: empty experts, one expert holding every row, segments of exactly 256 rows
-and of one row, fewer kept rows than the buffer holds.
+contiguous range of tiles (contiguous row map), on whole chunks dealt round-robin
+(chunked row map) or on an equal, contiguous share of every expert (shared row map,
+weight gradients); for the weight gradients it also walks the persistent launch (256, 64
+or 8 blocks, each stepping through the one-tile launch's blocks of its XCD until the
+first without a tile) and asserts the same exact-once coverage.  Offsets: each bf16
+layer shape routed by the oracle on router inputs drawn on the CPU (the same recipe and
+sizes as on the GPU; the CPU generator's values differ from the GPU's, so the segments
+are of the same distribution, not identical; the GPU test runs the same check on the
+device's own offsets), plus edge cases: empty experts, one expert holding every row,
+segments of exactly 256 rows and of one row, fewer kept rows than the buffer holds.
 """
 import os
 import shutil
@@ -42,7 +43,7 @@ def _run(exe, offsets, R, d, f):
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
     lines = r.stdout.strip().splitlines()
-    assert len(lines) == 18 and all(ln.endswith(" ok") for ln in lines), r.stdout
+    assert len(lines) == 26 and all(ln.endswith(" ok") for ln in lines), r.stdout
     return lines
 
 

@@ -153,7 +153,7 @@ struct GemmArgs {
     void* C1;
     void* C2;
     int out_f32;  // fwd down / dgrad gate/up: C0 is fp32 (partial sums over an f shard)
-    int row_share;  // row passes: which XCD runs which tile (tiles::row_tile), set by the launcher
+    int row_map;  // row passes: which XCD runs which tile (tiles::RowMap), set by the launcher
 };
 
 bool mfma_shape_ok(const moe_desc& d);

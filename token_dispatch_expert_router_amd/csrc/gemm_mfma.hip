@@ -56,8 +56,9 @@
 // Blocks are dispatched round-robin over the 8 XCDs; logical tiles are remapped so
 // that each XCD runs contiguous runs of tiles, in which consecutive tiles form 4 x 8
 // blocks (groups of four m-tiles, M fastest) whose operand panels stay in that XCD's L2:
-// either one contiguous eighth of all tiles or the same contiguous eighth of every
-// expert's tiles, chosen per launch by measurement (tiles::row_share).  The
+// one contiguous eighth of all tiles, chunks of 32 tiles dealt round-robin, or the same
+// contiguous eighth of every expert's tiles, chosen per launch by measurement
+// (tiles::row_map).  The
 // weight-gradient passes, whose tiles' K is their expert's segment length, always take
 // the latter; with short segments they run as one persistent block per CU that carries
 // the operand ring from tile to tile (gg_wgrad_kernel).
@@ -834,8 +835,8 @@ gg_mfma_kernel(GemmArgs g) {
     if (MODE <= GG_DGRAD_GATEUP) {
         const int n_tiles = tiles::row_n_tiles(MODE, d, f);
         int nt, mh;
-        if (!tiles::row_tile(blockIdx.x, g.offsets, g.E, n_tiles, HALF, g.row_share != 0, e, m0,
-                             m_lim, nt, mh))
+        if (!tiles::row_tile(blockIdx.x, g.offsets, g.E, n_tiles, HALF, g.row_map, e, m0, m_lim,
+                             nt, mh))
             return;
         half = mh < BM;
         n0 = nt * (MODE == GG_FWD_GATEUP ? 128 : BN);
@@ -1187,7 +1188,7 @@ bool mfma_shape_ok(const moe_desc& d) {
 
 hipError_t launch_gemm_mfma(GemmMode mode, const GemmArgs& args, hipStream_t s) {
     GemmArgs a = args;
-    a.row_share = tiles::row_share(mode, a.R, a.E) ? 1 : 0;
+    a.row_map = tiles::row_map(mode, a.R, a.E);
     const int64_t g8 = tiles::grid_blocks(mode, a.E, a.R, a.d, a.f);
     if (g8 <= 0) return hipSuccess;
     if (g8 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

@@ -61,25 +61,41 @@ __host__ __device__ __forceinline__ void row_extent(int lo, int hi, int mi, bool
     mh = (half && hi - m0 <= BM / 2) ? BM / 2 : BM;
 }
 
+// The row maps (which XCD runs which tile of a row pass), chosen per launch (row_map).
+enum RowMap { ROW_CONTIGUOUS = 0, ROW_SHARED = 1, ROW_CHUNKED = 2 };
+constexpr int CHUNK = 32;  // tiles per chunk of the chunked map: one XCD's tiles in flight
+
 // Row passes: (expert, first row, segment end, n-tile, tile height) of block b, false
-// for a block with no tile.  Two maps, chosen per launch (row_share):
-//  - contiguous: the tiles of all segments in order (each segment's in grouped order) are
-//    cut into eight equal contiguous ranges, one per XCD, so an XCD keeps one expert's
-//    row panels to itself;
+// for a block with no tile.  Block b runs the (b / 8)-th tile of XCD b % 8's sequence
+// under one of three maps of the logical tile order (the segments in order, each
+// segment's tiles in grouped order):
+//  - contiguous: the order is cut into eight equal contiguous ranges, one per XCD, so an
+//    XCD keeps its experts' row panels to itself;
+//  - chunked: the order is cut into chunks of CHUNK tiles dealt round-robin to the XCDs,
+//    so an XCD still runs 4 x 8 blocks while the eight XCDs run eight neighbouring
+//    chunks, the same expert's rows and adjacent weight columns, at the same time;
 //  - shared: XCD x takes the same contiguous eighth of every segment's tile order, tiles
 //    [x T / 8, (x + 1) T / 8) of a segment of T tiles, segment after segment, so all XCDs
-//    work on the same experts at the same time (the weight panels that several XCDs
-//    need are then fetched from HBM once and served to the others by the last-level
-//    cache) and each streams the same share of every expert's weights, however unequal
-//    the segments.
-// Block b runs the (b / 8)-th tile of XCD b % 8's sequence.
+//    work on the same experts at the same time (weight columns that several XCDs need
+//    for different row groups are fetched from HBM once and served to the others by the
+//    last-level cache) and each streams the same share of every expert's weights,
+//    however unequal the segments.
 __host__ __device__ __forceinline__ bool row_tile(int b, const int32_t* offsets, int E,
-                                                  int n_tiles, bool half, bool share, int& e,
+                                                  int n_tiles, bool half, int map, int& e,
                                                   int& m0, int& m_lim, int& nt, int& mh) {
     int mi;
-    if (!share) {
-        const int L = xcd_remap(b, count_row_tiles(offsets, E) * n_tiles);
-        if (L < 0) return false;
+    const int x = b % NXCD;
+    const int j = b / NXCD;
+    if (map != ROW_SHARED) {
+        const int valid = count_row_tiles(offsets, E) * n_tiles;
+        int L;
+        if (map == ROW_CHUNKED) {
+            L = ((j / CHUNK) * NXCD + x) * CHUNK + j % CHUNK;
+            if (L >= valid) return false;
+        } else {
+            L = xcd_remap(b, valid);
+            if (L < 0) return false;
+        }
         int acc = 0;
         for (int i = 0; i < E; ++i) {
             const int lo = offsets[i], hi = offsets[i + 1];
@@ -96,8 +112,6 @@ __host__ __device__ __forceinline__ bool row_tile(int b, const int32_t* offsets,
         }
         return false;
     }
-    const unsigned x = (unsigned)b % NXCD;
-    const int j = b / NXCD;
     int acc = 0;
     for (int i = 0; i < E; ++i) {
         const int lo = offsets[i], hi = offsets[i + 1];
@@ -118,17 +132,21 @@ __host__ __device__ __forceinline__ bool row_tile(int b, const int32_t* offsets,
 }
 
 // Which row map a launch takes, by measurement on the layer shapes (R rows of buffer
-// bound over E experts): with more than 1024 rows per expert (two or more groups of
-// four m-tiles) the shared map on every row pass (forward and dgrads 4-8% faster: the
-// XCDs that run the same weight columns for different row groups do so at the same
-// time); with 641-1024 rows the shared map on all but the down forward pass (the dgrads
-// 4% faster, the down forward 4% slower); with at most 640 rows (one or two m-tiles per
-// expert, whose row panels the shared map sends to all eight XCDs) only on the gate/up
-// forward pass, whose half-height last tiles otherwise leave the XCDs unequal work (5%).
-__host__ __forceinline__ bool row_share(int mode, int64_t R, int E) {
-    if (mode == GG_FWD_GATEUP) return true;
-    if (mode == GG_FWD_DOWN) return R > 1024LL * E;
-    return R > 640LL * E;
+// bound over E experts; kernel traces, the three maps in turn on one MI355X):
+//  - more than 1024 rows per expert (two or more groups of four m-tiles): shared on every
+//    row pass (4-8% faster than contiguous, 1-3% faster than chunked);
+//  - 641-1024 rows (one group of four m-tiles): chunked for the forward passes (3% faster
+//    than contiguous; shared makes the down forward 5% slower) and shared for the dgrads
+//    (3-4% faster than contiguous, the gate/up dgrad 3% faster than chunked);
+//  - at most 640 rows (one or two m-tiles per expert, whose row panels the shared and
+//    chunked maps send to several XCDs): shared for the gate/up forward, whose
+//    half-height last tiles otherwise leave the XCDs unequal work (6% faster), and
+//    contiguous for the other passes (the dgrads 4-8% slower otherwise).
+__host__ __forceinline__ int row_map(int mode, int64_t R, int E) {
+    if (R > 1024LL * E) return ROW_SHARED;
+    const bool fwd = mode == GG_FWD_GATEUP || mode == GG_FWD_DOWN;
+    if (R > 640LL * E) return fwd ? ROW_CHUNKED : ROW_SHARED;
+    return mode == GG_FWD_GATEUP ? ROW_SHARED : ROW_CONTIGUOUS;
 }
 
 // n-tiles of a row-segmented pass (modes GG_FWD_GATEUP .. GG_DGRAD_GATEUP).
@@ -164,10 +182,12 @@ __host__ __device__ __forceinline__ bool wgrad_tile(int b, int E, int MT, int NT
 }
 
 // Blocks a pass launches (a multiple of 8): row passes are sized for the worst case of
-// ceil(R / 256) + E m-tiles (the real counts live on the device), with the shared map
-// plus E blocks per XCD for the rounding of each segment's eighth up to whole tiles; the
-// weight gradients for ceil(per / 8) tiles of each expert on every XCD.
-__host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, int f) {
+// ceil(R / 256) + E m-tiles (the real counts live on the device), rounded up to whole
+// rounds of eight chunks with the chunked map and plus E blocks per XCD (the rounding of
+// each segment's eighth up to whole tiles) with the shared map; the weight gradients for
+// ceil(per / 8) tiles of each expert on every XCD.  `map` < 0: the map row_map picks.
+__host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, int f,
+                                             int map = -1) {
     int64_t tiles;
     if (mode == GG_WGRAD_DOWN || mode == GG_WGRAD_GATEUP) {
         int MT, NT;
@@ -175,8 +195,10 @@ __host__ __forceinline__ int64_t grid_blocks(int mode, int E, int64_t R, int d, 
         tiles = (int64_t)E * (((int64_t)MT * NT + NXCD - 1) / NXCD) * NXCD;
     } else {
         const int64_t mt_max = (R + BM - 1) / BM + E;
-        tiles = (mt_max * row_n_tiles(mode, d, f) + NXCD - 1) / NXCD * NXCD;
-        if (row_share(mode, R, E)) tiles += (int64_t)NXCD * E;
+        tiles = mt_max * row_n_tiles(mode, d, f);
+        if (map < 0) map = row_map(mode, R, E);
+        if (map == ROW_CHUNKED) tiles = (tiles + NXCD * CHUNK - 1) / (NXCD * CHUNK) * (NXCD * CHUNK);
+        if (map == ROW_SHARED) tiles = (tiles + NXCD - 1) / NXCD * NXCD + (int64_t)NXCD * E;
     }
     return (tiles + NXCD - 1) / NXCD * NXCD;
 }
