@@ -98,6 +98,11 @@ CASES = {
                        w_std=0.05),
     # every expert chosen by every token (K = E): the gates are the whole softmax
     "k_eq_e": _shape("k_eq_e", T=256, d=256, E=4, K=4, f=256, seed=36, w_std=0.05),
+    # fp32, two experts, sharp gates (one gate within a few ulps of 1 for some tokens) and
+    # heavy drops: the router gradient g (dgate - sum g dgate) cancels, which fp32
+    # arithmetic held only to 1.1e-5 of the largest dlogit here (now formed in fp64)
+    "f32_sharp_gates": _shape("f32_sharp_gates", T=492, d=224, E=2, K=2, f=120, seed=342,
+                              dtype="f32", cf=0.27, sub_seq=123, w_std=0.05, wr_std=0.5),
     # a single 16-token router block and sub-sequence
     "t16": _shape("t16", T=16, d=256, E=8, K=2, f=256, sub_seq=16, cf=1.0, seed=37, w_std=0.05),
     # two segments of about 1024 rows: four m-tiles each, one full group of the grouped

@@ -257,8 +257,10 @@ __global__ void __launch_bounds__(256) unpermute_bwd_kernel(
         if (lane == 0) dgate[t * K + k] = v;
     }
     if (shared) {
+        // sigma'(z) = sigma(z) sigma(-z): 1 - s would lose the leading bits of sigma(-z)
+        // when s is close to 1
         const float v = wave_sum(sdot);
-        if (lane == 0) dz[t] = v * s * (1.f - s);
+        if (lane == 0) dz[t] = v * s * sigmoid_f(-z[t]);
     }
 }
 
@@ -507,7 +509,12 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
     }
 }
 
-// dl for the K chosen experts: g_j (dgate_j - sum_k g_k dgate_k); 0 elsewhere.
+// dl for the K chosen experts: g_j (dgate_j - sum_k g_k dgate_k); 0 elsewhere.  The
+// difference cancels when one gate is close to 1 (dgate_j - g_j dgate_j - ...), so it is
+// formed in fp64: the products of two fp32 values are exact there, and dl is then
+// correct to its own fp32 rounding (in fp32 the difference kept an absolute error of
+// about one ulp of dgate_j, a relative error of up to 1e-4 on dl at g_j near 1).  K
+// values per token: the fp64 cost is negligible.
 __global__ void __launch_bounds__(256) dlogits_kernel(const int32_t* __restrict__ topk_idx,
                                                       const float* __restrict__ gate,
                                                       const float* __restrict__ dgate, int T,
@@ -515,11 +522,12 @@ __global__ void __launch_bounds__(256) dlogits_kernel(const int32_t* __restrict_
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    float inner = 0.f;
-    for (int k = 0; k < K; ++k) inner += gate[t * K + k] * dgate[t * K + k];
+    double inner = 0.0;
+    for (int k = 0; k < K; ++k) inner += (double)gate[t * K + k] * (double)dgate[t * K + k];
     float v = 0.f;
     for (int k = 0; k < K; ++k)
-        if (topk_idx[t * K + k] == lane) v = gate[t * K + k] * (dgate[t * K + k] - inner);
+        if (topk_idx[t * K + k] == lane)
+            v = (float)((double)gate[t * K + k] * ((double)dgate[t * K + k] - inner));
     if (lane < E) dl[t * E + lane] = v;
 }
 
