@@ -68,6 +68,10 @@ CASES = {
     # the same on the vector-ALU router (d not a multiple of 128)
     "shared_e64_valu": _shape("shared_e64_valu", T=128, d=200, E=64, K=4, f=136, fs=72, sub_seq=128,
                               seed=20, w_std=0.05),
+    # fp32 with a shared expert and sharp gates: the shared gate's derivative and every
+    # shared-expert output and gradient held to the fp32 bound
+    "fp32_shared": _shape("fp32_shared", T=320, d=96, E=8, K=2, f=64, fs=48, sub_seq=160,
+                          cf=1.0, seed=39, dtype="f32", w_std=0.05, wr_std=0.5),
     # fp32 with 16 experts (the router weight gradient's many-column kernel, in fp32)
     "fp32_e16": _shape("fp32_e16", T=192, d=72, E=16, K=4, f=40, sub_seq=64, cf=1.0, seed=21,
                        dtype="f32", w_std=None, wr_std=0.5),
@@ -268,11 +272,14 @@ def _random_shapes(n=24, seed=2024):
     384 or 640 takes the matrix-core router with four waves per block and the vector-ALU
     GEMMs) or of 8 (vector-ALU router and GEMMs), and some fp32 layers; E up to 64 with K up
     to 8, dropless or cf in (0.25, 2], one to four sub-sequences, an optional shared
-    expert."""
+    expert (on every kind; the vector-ALU and fp32 layers draw theirs from a second
+    generator, so the other draws keep their values)."""
     rng = np.random.default_rng(seed)
+    rng_fs = np.random.default_rng(seed + 1)
     out = []
     for i in range(n):
         kind = int(rng.integers(0, 5))  # 0-1 matrix cores, 2 four-wave router, 3 VALU, 4 fp32
+        fs_other = int(8 * rng_fs.integers(4, 40)) if rng_fs.random() < 1 / 3 else 0
         mfma = kind <= 1
         if mfma:
             d = int(rng.choice([256, 512]))
@@ -286,7 +293,7 @@ def _random_shapes(n=24, seed=2024):
         n_sub = int(rng.integers(1, 5))
         S = int(rng.integers(16, 160))
         cf = None if rng.random() < 0.3 else float(np.round(rng.uniform(0.25, 2.0), 2))
-        fs = int(rng.choice([0, 0, 256])) if mfma else 0
+        fs = int(rng.choice([0, 0, 256])) if mfma else fs_other
         dtype = "f32" if kind == 4 else "bf16"
         out.append(_shape(f"rand{i}", T=n_sub * S, d=d, E=E, K=K, f=f, sub_seq=S, cf=cf, fs=fs,
                           seed=100 + i, w_std=0.05, wr_std=0.5, dtype=dtype))
