@@ -273,13 +273,15 @@ def _random_shapes(n=24, seed=2024):
     GEMMs) or of 8 (vector-ALU router and GEMMs), and some fp32 layers; E up to 64 with K up
     to 8, dropless or cf in (0.25, 2], one to four sub-sequences, an optional shared
     expert (on every kind; the vector-ALU and fp32 layers draw theirs from a second
-    generator, so the other draws keep their values)."""
+    generator, so the other draws keep their values) and, from that generator too, an
+    optional skewed router bias."""
     rng = np.random.default_rng(seed)
     rng_fs = np.random.default_rng(seed + 1)
     out = []
     for i in range(n):
         kind = int(rng.integers(0, 5))  # 0-1 matrix cores, 2 four-wave router, 3 VALU, 4 fp32
         fs_other = int(8 * rng_fs.integers(4, 40)) if rng_fs.random() < 1 / 3 else 0
+        zipf = bool(rng_fs.random() < 0.2)
         mfma = kind <= 1
         if mfma:
             d = int(rng.choice([256, 512]))
@@ -296,7 +298,7 @@ def _random_shapes(n=24, seed=2024):
         fs = int(rng.choice([0, 0, 256])) if mfma else fs_other
         dtype = "f32" if kind == 4 else "bf16"
         out.append(_shape(f"rand{i}", T=n_sub * S, d=d, E=E, K=K, f=f, sub_seq=S, cf=cf, fs=fs,
-                          seed=100 + i, w_std=0.05, wr_std=0.5, dtype=dtype))
+                          seed=100 + i, w_std=0.05, wr_std=0.5, dtype=dtype, zipf_bias=zipf))
     return out
 
 
